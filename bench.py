@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Training-step benchmark of the bitwise-reproducible FP32 decoder on one MI355X.
+
+A step is one optimizer step of the whole hot path: for each micro-batch, the
+forward pass with cross-entropy and the backward pass folding its gradient into
+the accumulator, then AdamW. The default workload is the 162,147,840-parameter
+decoder of the MojoLearn 162M model card (12 layers, d 768, 12 heads x 64,
+SwiGLU 2048, untied 50,257 tables) with 64 micro-batches of 4 x 2,048 synthetic
+Zipf(1.1) token ids per step (524,288 tokens). All token ids of the timed
+steps are uploaded to HBM before timing starts.
+
+Prints one JSON line: tokens/s, the step's FP32 TFLOP/s against the MI355X
+peak, the roofline of the dominant contraction kernel (HIP events around every
+launch inside the timed region, grouped by kernel), and the CPU oracle's rate on
+this host's cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/s + FP32 TFLOP/s %peak at 162M (1 GPU), bit-exact vs oracle"
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def flops_per_token(cfg: dict) -> float:
+    """Algorithmic FLOPs per token of one training step: 6 per parameter of the
+    matrix products (forward 2, backward 4) plus the causal attention pairs."""
+    d, F, L, V, T = cfg["d_model"], cfg["ffn_hidden"], cfg["n_layers"], cfg["vocab"], cfg["seq_len"]
+    p_mm = L * (4 * d * d + 3 * d * F) + V * d
+    return 6.0 * p_mm + 6.0 * L * d * (T + 1)
+
+
+def cpu_baseline(cfg_name: str, init: np.ndarray, seconds_hint: float) -> dict:
+    """The oracle as it stands, on a bounded sample of the workload: one
+    forward+backward of a 1 x 512-token micro-batch of the same model, with
+    OpenMP across independent outputs on this host's cores. The rate is scaled
+    to tokens/s of the benchmark workload by FLOPs per token."""
+    import oracle
+    from bitwise_reproducible_fp32_amd import inputs as I
+    cfg = I.make_config(cfg_name)
+    T = min(512, cfg["seq_len"])
+    scfg = dict(cfg, batch=1, seq_len=T)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    oracle.set_threads(cores)
+    m = oracle.Model(scfg, init)
+    if cfg_name == "c0":
+        x, y = I.c0_batch(0, 1, T)
+    else:
+        w = I.zipf_ids(T + 1, cfg["vocab"], [9, 0])
+        x, y = w[:T], w[1:]
+    t0 = time.perf_counter()
+    m.forward(x, y)
+    m.backward()
+    dt = time.perf_counter() - t0
+    sample_flops = flops_per_token(scfg) * T
+    rate = sample_flops / dt
+    return {"value": rate / flops_per_token(cfg), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle forward+backward of one 1x{T}-token micro-batch of the {cfg_name} model "
+                      f"({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s), scaled by FLOPs per token of the workload",
+            "gflops": rate / 1e9, "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c4", choices=["c0", "c3", "c4"])
+    ap.add_argument("--micro", type=int, default=0, help="micro-batches per step (default: the config's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; the data-parallel path over several "
+                                   "GPUs is a design (DESIGN.md), not implemented", "n_gpus": a.gpus}))
+        return 2
+
+    import torch
+
+    import bitwise_reproducible_fp32_amd as mlb
+    from bitwise_reproducible_fp32_amd import inputs as I
+
+    cfg = I.make_config(a.config)
+    if a.micro:
+        cfg["micro"] = a.micro
+    S, B, T = cfg["micro"], cfg["batch"], cfg["seq_len"]
+    t_setup = time.perf_counter()
+    init = I.init_params(cfg)
+    torch.cuda.set_device(0)
+    model = mlb.Model(cfg, init)
+    nsteps = a.warmup + a.steps
+    xs = np.empty((nsteps, S, B * T), np.int32)
+    ys = np.empty_like(xs)
+    for s in range(nsteps):
+        for mb in range(S):
+            x, y = I.batch_for(a.config, cfg, s + 1, mb)
+            xs[s, mb], ys[s, mb] = x.ravel(), y.ravel()
+    xd, yd = torch.from_numpy(xs).cuda(), torch.from_numpy(ys).cuda()
+    lrs = [I.lr_at(a.config, s + 1) for s in range(nsteps)]
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s; workspace {mlb.workspace_bytes(cfg) / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+
+    losses = []
+
+    def step(s: int) -> None:
+        for mb in range(S):
+            losses.append(float(model.forward_loss(xd[s, mb], yd[s, mb])))
+            model.backward()
+        model.adamw_step(lrs[s])
+
+    for s in range(a.warmup):
+        t0 = time.perf_counter()
+        step(s)
+        torch.cuda.synchronize()
+        print(f"# warmup step {s + 1}: {time.perf_counter() - t0:.2f}s", file=sys.stderr, flush=True)
+    model.stats_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.warmup, nsteps):
+        ts = time.perf_counter()
+        step(s)
+        print(f"# step {s + 1}: {time.perf_counter() - ts:.2f}s loss {losses[-1]:.5f}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stats = model.stats()
+    model.stats_enable(False)
+
+    tokens = S * B * T
+    fpt = flops_per_token(cfg)
+    value = tokens * a.steps / elapsed
+    tflops = fpt * tokens * a.steps / elapsed / 1e12
+
+    # dominant kernel: the contraction instantiation with the most time
+    by_kernel: dict[str, dict] = {}
+    for st in stats:
+        if st["flops"] > 0:
+            k = by_kernel.setdefault(st["kernel"], dict(ms=0.0, flops=0.0, launches=0, sites=set()))
+            k["ms"] += st["ms"]; k["flops"] += st["flops"]; k["launches"] += st["launches"]; k["sites"].add(st["site"])
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
+    dom_avg_ms = dom["ms"] / dom["launches"]
+    dom_achieved = dom["flops"] / dom["launches"] / (dom_avg_ms / 1e3) / 1e12
+    gemm_ms = sum(k["ms"] for k in by_kernel.values())
+    gemm_flops = sum(k["flops"] for k in by_kernel.values())
+    total_ms = sum(st["ms"] for st in stats)
+    mem_sites = {}
+    for st in stats:
+        if st["bytes"] > 0:
+            r = mem_sites.setdefault(st["site"], dict(ms=0.0, bytes=0.0, launches=0))
+            r["ms"] += st["ms"]; r["bytes"] += st["bytes"]; r["launches"] += st["launches"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed / a.steps * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Zipf(1.1) token ids, N(0,0.02) init)",
+        "config": {"workload": f"{a.config}: {I.param_count(cfg):,}-param decoder, {S} micro-batches of "
+                               f"{B}x{T} tokens per step", "tokens_per_step": tokens, "micro_batches": S,
+                   "batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "tflops": round(tflops, 2),
+        "pct_fp32_peak": round(100 * tflops / PEAK_FP32_TFLOPS, 2),
+        "flops_per_token": fpt,
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_achieved, 2),
+                     "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(dom_avg_ms, 4), "launches": dom["launches"],
+                     "flops_per_launch": dom["flops"] / dom["launches"], "sites": sorted(dom["sites"])},
+        "contractions": {"ms_share": round(gemm_ms / total_ms, 4) if total_ms else None,
+                         "tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 2) if gemm_ms else None},
+        "hbm_kernels": {k: {"GB/s": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1), "ms": round(v["ms"], 3)}
+                        for k, v in sorted(mem_sites.items(), key=lambda kv: -kv[1]["ms"])[:8]},
+        "loss_first_last": [losses[0], losses[-1]],
+    }
+    if not a.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(a.config, init, 20.0)
+        except Exception as e:  # the baseline is reported, never required
+            out["cpu_baseline"] = {"error": str(e)}
+    print(json.dumps(out), flush=True)
+    model.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

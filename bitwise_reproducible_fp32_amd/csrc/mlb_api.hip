@@ -1,0 +1,1074 @@
+// C-ABI host side: configuration checks and named refusals, arena planning,
+// the kernel sequence of one micro-batch, AdamW, and exact state bytes.
+//
+// The sequence follows the decoder of the MojoLearn 162M model card
+// (pre-norm RMSNorm, rotary attention, SwiGLU, no final norm, untied tables)
+// and its "Training" table (shard gradients summed in a fixed order, AdamW with
+// beta (0.9, 0.95), eps 1e-8, weight decay 0.1). The bit-level rules (MLB-P1)
+// live with the kernels; the host only orders launches and never does
+// arithmetic on tensor data, except the three scalars it hands to kernels:
+// 1/N, the attention scale RN(1/sqrt(hd)) and the AdamW bias corrections
+// RN(1 - beta^t) with beta^t a binary64 product of the binary32 beta.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/mlb.h"
+#include "../../include/mlb_prim.h"
+#include "mlb_internal.hpp"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+mlb_status fail(mlb_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+#define HIPCHK(x)                                                                                \
+    do {                                                                                         \
+        hipError_t e_ = (x);                                                                     \
+        if (e_ != hipSuccess) return fail(MLB_E_DEVICE, "%s: %s", #x, hipGetErrorString(e_)); \
+    } while (0)
+#define KCHK(x)                                                             \
+    do {                                                                    \
+        int r_ = (x);                                                       \
+        if (r_ != 0) return fail(MLB_E_DEVICE, "%s returned %d", #x, r_); \
+    } while (0)
+
+// ------------------------------------------------------------------ SHA-256
+// FIPS 180-4, written for this library (state bytes and their digests).
+class Sha {
+public:
+    Sha() { reset(); }
+    void reset() {
+        static const uint32_t h0[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au,
+                                       0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u};
+        for (int i = 0; i < 8; ++i) st_[i] = h0[i];
+        nbytes_ = 0;
+        used_ = 0;
+    }
+    void add(const void* data, size_t n) {
+        const uint8_t* p = static_cast<const uint8_t*>(data);
+        nbytes_ += n;
+        if (used_) {
+            while (n && used_ < 64) { blk_[used_++] = *p++; --n; }
+            if (used_ == 64) { compress(blk_); used_ = 0; }
+        }
+        while (n >= 64) { compress(p); p += 64; n -= 64; }
+        while (n) { blk_[used_++] = *p++; --n; }
+    }
+    void digest(uint8_t out[32]) {
+        const uint64_t bits = nbytes_ * 8u;
+        const uint8_t one = 0x80, zero = 0;
+        add(&one, 1);
+        while (used_ != 56) add(&zero, 1);
+        uint8_t len[8];
+        for (int i = 0; i < 8; ++i) len[i] = (uint8_t)(bits >> (8 * (7 - i)));
+        add(len, 8);
+        for (int i = 0; i < 8; ++i)
+            for (int b = 0; b < 4; ++b) out[4 * i + b] = (uint8_t)(st_[i] >> (24 - 8 * b));
+    }
+
+private:
+    static uint32_t ror(uint32_t x, unsigned r) { return (x >> r) | (x << (32u - r)); }
+    void compress(const uint8_t* p) {
+        static const uint32_t k[64] = {
+            0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u, 0xab1c5ed5u,
+            0xd807aa98u, 0x12835b01u, 0x243185beu, 0x550c7dc3u, 0x72be5d74u, 0x80deb1feu, 0x9bdc06a7u, 0xc19bf174u,
+            0xe49b69c1u, 0xefbe4786u, 0x0fc19dc6u, 0x240ca1ccu, 0x2de92c6fu, 0x4a7484aau, 0x5cb0a9dcu, 0x76f988dau,
+            0x983e5152u, 0xa831c66du, 0xb00327c8u, 0xbf597fc7u, 0xc6e00bf3u, 0xd5a79147u, 0x06ca6351u, 0x14292967u,
+            0x27b70a85u, 0x2e1b2138u, 0x4d2c6dfcu, 0x53380d13u, 0x650a7354u, 0x766a0abbu, 0x81c2c92eu, 0x92722c85u,
+            0xa2bfe8a1u, 0xa81a664bu, 0xc24b8b70u, 0xc76c51a3u, 0xd192e819u, 0xd6990624u, 0xf40e3585u, 0x106aa070u,
+            0x19a4c116u, 0x1e376c08u, 0x2748774cu, 0x34b0bcb5u, 0x391c0cb3u, 0x4ed8aa4au, 0x5b9cca4fu, 0x682e6ff3u,
+            0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau, 0xa4506cebu, 0xbef9a3f7u, 0xc67178f2u};
+        uint32_t w[64];
+        for (int t = 0; t < 16; ++t)
+            w[t] = ((uint32_t)p[4 * t] << 24) | ((uint32_t)p[4 * t + 1] << 16) | ((uint32_t)p[4 * t + 2] << 8) |
+                   (uint32_t)p[4 * t + 3];
+        for (int t = 16; t < 64; ++t)
+            w[t] = (ror(w[t - 2], 17) ^ ror(w[t - 2], 19) ^ (w[t - 2] >> 10)) + w[t - 7] +
+                   (ror(w[t - 15], 7) ^ ror(w[t - 15], 18) ^ (w[t - 15] >> 3)) + w[t - 16];
+        uint32_t v[8];
+        for (int i = 0; i < 8; ++i) v[i] = st_[i];
+        for (int t = 0; t < 64; ++t) {
+            const uint32_t t1 = v[7] + (ror(v[4], 6) ^ ror(v[4], 11) ^ ror(v[4], 25)) +
+                                ((v[4] & v[5]) ^ (~v[4] & v[6])) + k[t] + w[t];
+            const uint32_t t2 = (ror(v[0], 2) ^ ror(v[0], 13) ^ ror(v[0], 22)) +
+                                ((v[0] & v[1]) ^ (v[0] & v[2]) ^ (v[1] & v[2]));
+            for (int i = 7; i > 0; --i) v[i] = v[i - 1];
+            v[4] += t1;
+            v[0] = t1 + t2;
+        }
+        for (int i = 0; i < 8; ++i) st_[i] += v[i];
+    }
+    uint32_t st_[8];
+    uint8_t blk_[64];
+    uint64_t nbytes_;
+    size_t used_;
+};
+
+void sha256_bytes(const void* p, size_t n, uint8_t out[32]) {
+    Sha s;
+    s.add(p, n);
+    s.digest(out);
+}
+
+// ------------------------------------------------------------ layout
+constexpr size_t ALIGN = 256;
+constexpr int64_t KCH = 1024;
+constexpr int64_t MAX_TOKENS = 8192;
+
+struct Sizes {
+    int64_t V, d, L, H, hd, F, B, T, N, P;
+    bool tied;
+};
+
+bool cfg_valid(const mlb_config* c, std::string* why) {
+    if (!c) { *why = "config is null"; return false; }
+    if (c->abi_version != MLB_ABI_VERSION) { *why = "abi_version mismatch"; return false; }
+    if (!c->vocab || !c->d_model || !c->n_layers || !c->n_heads || !c->head_dim || !c->ffn_hidden || !c->batch ||
+        !c->seq_len) { *why = "zero-sized dimension"; return false; }
+    if ((uint64_t)c->n_heads * c->head_dim != c->d_model) { *why = "d_model != n_heads * head_dim"; return false; }
+    if (c->tied > 1) { *why = "tied must be 0 or 1"; return false; }
+    const float f[6] = {c->rope_theta, c->rms_eps, c->beta1, c->beta2, c->adam_eps, c->weight_decay};
+    for (float x : f)
+        if (!std::isfinite(x)) { *why = "non-finite hyper-parameter"; return false; }
+    return true;
+}
+
+// Shapes the kernels are not built for: a named refusal, never a slower path.
+bool cfg_supported(const mlb_config* c, std::string* why) {
+    if (c->head_dim % 2) { *why = "rotary pairs need an even head_dim"; return false; }
+    if (c->d_model % 32 || c->ffn_hidden % 32) { *why = "d_model and ffn_hidden must be multiples of 32"; return false; }
+    if ((uint64_t)c->batch * c->seq_len > (uint64_t)MAX_TOKENS) {
+        *why = "more than 8192 tokens per micro-batch";
+        return false;
+    }
+    if (c->vocab > 0x7fffffffu) { *why = "vocab too large"; return false; }
+    return true;
+}
+
+Sizes sizes_of(const mlb_config* c) {
+    Sizes s;
+    s.V = c->vocab; s.d = c->d_model; s.L = c->n_layers; s.H = c->n_heads; s.hd = c->head_dim;
+    s.F = c->ffn_hidden; s.B = c->batch; s.T = c->seq_len; s.N = s.B * s.T; s.tied = c->tied != 0;
+    s.P = s.V * s.d + s.L * (2 * s.d + 4 * s.d * s.d + 3 * s.F * s.d) + (s.tied ? 0 : s.V * s.d);
+    return s;
+}
+
+// Arena carve-up; the same walk sizes the arena and assigns the pointers.
+struct Carve {
+    char* base;
+    size_t off = 0;
+    template <class T> T* take(int64_t n) {
+        off = (off + ALIGN - 1) / ALIGN * ALIGN;
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += (size_t)n * sizeof(T);
+        return p;
+    }
+};
+
+int64_t split_floats(const Sizes& s) {
+    // per-chunk partials of the weight-gradient contractions over N tokens
+    mlb::GemmPlan auto_plan;
+    int64_t best = 0;
+    const int64_t shapes[6][3] = {{3 * s.d, s.d, s.N}, {s.d, s.d, s.N}, {2 * s.F, s.d, s.N},
+                                  {s.d, s.F, s.N},     {s.V, s.d, s.N}, {s.N, s.d, s.V}};
+    for (const auto& sh : shapes) {
+        mlb::GemmDesc g;
+        g.M = sh[0]; g.N = sh[1]; g.K = sh[2]; g.kseg = sh[2];
+        int64_t f = mlb::gemm_split_scratch(g, auto_plan);
+        if (f > best) best = f;
+    }
+    return best;
+}
+
+}  // namespace
+
+struct StatRec {
+    std::string site, kernel;
+    double flops = 0, bytes = 0;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+};
+struct StatAgg {
+    std::string site, kernel;
+    int64_t launches = 0;
+    double ms = 0, flops = 0, bytes = 0;
+};
+
+struct mlb_model {
+    mlb_config cfg;
+    Sizes s;
+    hipStream_t stream;
+    int device;
+    // parameter offsets (floats)
+    int64_t offE, offOut;
+    std::vector<int64_t> o_w1, o_qkv, o_wo, o_w2, o_gu, o_wd;
+    // state
+    float *p, *G, *m, *v;
+    float *cosv, *sinv;
+    int32_t *ids, *tg;
+    int* err;
+    float* loss_dev;
+    float* loss_rows;
+    std::vector<float*> h, xn1, r1, qkv, P, O, hmid, xn2, r2, gu, a;   // h has L+1 entries
+    float* logits;
+    float *dh, *dA, *dgu, *dxn, *dO, *dqkv, *dP, *Dv, *gE, *split, *dwpart;
+    int64_t split_n;
+    uint64_t* keys;
+    float* host_stage;   // pinned, 64 bytes
+    uint64_t step;
+    bool have_fwd;
+    int n_accum;
+    float attn_scale, invN;
+    bool stats_on = false;
+    std::vector<StatRec> pending;
+    std::vector<hipEvent_t> free_events;
+    std::map<std::string, StatAgg> agg;
+};
+
+namespace {
+
+size_t carve(mlb_model* M, char* base) {
+    const Sizes& s = M->s;
+    Carve c{base};
+    M->p = c.take<float>(s.P);
+    M->G = c.take<float>(s.P);
+    M->m = c.take<float>(s.P);
+    M->v = c.take<float>(s.P);
+    M->cosv = c.take<float>(s.T * s.hd / 2);
+    M->sinv = c.take<float>(s.T * s.hd / 2);
+    M->ids = c.take<int32_t>(s.N);
+    M->tg = c.take<int32_t>(s.N);
+    M->err = c.take<int>(64);
+    M->loss_dev = c.take<float>(64);
+    M->loss_rows = c.take<float>(s.N);
+    M->h.assign(s.L + 1, nullptr);
+    for (auto* vec : {&M->xn1, &M->r1, &M->qkv, &M->P, &M->O, &M->hmid, &M->xn2, &M->r2, &M->gu, &M->a})
+        vec->assign(s.L, nullptr);
+    for (int64_t l = 0; l <= s.L; ++l) M->h[l] = c.take<float>(s.N * s.d);
+    for (int64_t l = 0; l < s.L; ++l) {
+        M->xn1[l] = c.take<float>(s.N * s.d);
+        M->r1[l] = c.take<float>(s.N);
+        M->qkv[l] = c.take<float>(s.N * 3 * s.d);
+        M->P[l] = c.take<float>(s.B * s.H * s.T * s.T);
+        M->O[l] = c.take<float>(s.N * s.d);
+        M->hmid[l] = c.take<float>(s.N * s.d);
+        M->xn2[l] = c.take<float>(s.N * s.d);
+        M->r2[l] = c.take<float>(s.N);
+        M->gu[l] = c.take<float>(s.N * 2 * s.F);
+        M->a[l] = c.take<float>(s.N * s.F);
+    }
+    M->logits = c.take<float>(s.N * s.V);
+    M->dh = c.take<float>(s.N * s.d);
+    M->dA = c.take<float>(s.N * s.F);
+    M->dgu = c.take<float>(s.N * 2 * s.F);
+    M->dxn = c.take<float>(s.N * s.d);
+    M->dO = c.take<float>(s.N * s.d);
+    M->dqkv = c.take<float>(s.N * 3 * s.d);
+    M->dP = c.take<float>(s.B * s.H * s.T * s.T);
+    M->Dv = c.take<float>(s.B * s.H * s.T);
+    M->gE = s.tied ? c.take<float>(s.V * s.d) : nullptr;
+    M->split_n = split_floats(s);
+    M->split = c.take<float>(M->split_n > 0 ? M->split_n : 1);
+    M->dwpart = c.take<float>(((s.N + KCH - 1) / KCH) * s.d);
+    M->keys = c.take<uint64_t>(2 * MAX_TOKENS);
+    return c.off + ALIGN;
+}
+
+void offsets(mlb_model* M) {
+    const Sizes& s = M->s;
+    int64_t o = 0;
+    M->offE = o; o += s.V * s.d;
+    for (int64_t l = 0; l < s.L; ++l) {
+        M->o_w1.push_back(o); o += s.d;
+        M->o_qkv.push_back(o); o += 3 * s.d * s.d;
+        M->o_wo.push_back(o); o += s.d * s.d;
+        M->o_w2.push_back(o); o += s.d;
+        M->o_gu.push_back(o); o += 2 * s.F * s.d;
+        M->o_wd.push_back(o); o += s.d * s.F;
+    }
+    M->offOut = s.tied ? M->offE : o;
+}
+
+// RoPE table: cos/sin of t * theta^(-2i/hd), binary64 on the host, rounded.
+void rope_table_host(int64_t T, int64_t hd, float theta, std::vector<float>& c, std::vector<float>& sn) {
+    const int64_t h2 = hd / 2;
+    c.resize(T * h2);
+    sn.resize(T * h2);
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < h2; ++i) {
+            const double ex = -(2.0 * (double)i) / (double)hd;
+            const double ang = (double)t * std::pow((double)theta, ex);
+            c[t * h2 + i] = (float)std::cos(ang);
+            sn[t * h2 + i] = (float)std::sin(ang);
+        }
+}
+
+float bias_corr(float beta, uint64_t t) {
+    double b = 1.0;
+    for (uint64_t i = 0; i < t; ++i) b *= (double)beta;
+    return (float)(1.0 - b);
+}
+
+mlb::GemmDesc lin(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, bool akc, const float* B,
+                  int64_t ldb, bool bkc, float* C, int64_t ldc, int mode) {
+    mlb::GemmDesc g;
+    g.M = M; g.N = N; g.K = K; g.kseg = K;
+    g.A = A; g.lda = lda; g.a_kc = akc;
+    g.B = B; g.ldb = ldb; g.b_kc = bkc;
+    g.C = C; g.ldc = ldc; g.mode = mode;
+    return g;
+}
+
+// ------------------------------------------------------------ launch stats
+// Optional per-launch timing with HIP events on the model's stream, grouped by
+// call site, with each launch's algorithmic work (FLOPs of the contraction's
+// valid pairs, or the minimal HBM bytes of a row/elementwise kernel).
+int64_t stat_begin(mlb_model* M) {
+    if (!M->stats_on) return -1;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (M->free_events.size() >= 2) {
+        e0 = M->free_events.back(); M->free_events.pop_back();
+        e1 = M->free_events.back(); M->free_events.pop_back();
+    } else {
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1;
+    }
+    if (hipEventRecord(e0, M->stream) != hipSuccess) return -1;
+    StatRec r;
+    r.e0 = e0; r.e1 = e1;
+    M->pending.push_back(r);
+    return (int64_t)M->pending.size() - 1;
+}
+
+void stat_end(mlb_model* M, int64_t idx, const char* site, const char* kernel, double flops, double bytes) {
+    if (idx < 0) return;
+    StatRec& r = M->pending[(size_t)idx];
+    (void)hipEventRecord(r.e1, M->stream);
+    r.site = site; r.kernel = kernel; r.flops = flops; r.bytes = bytes;
+}
+
+// Call only after the stream is synchronised.
+void stat_resolve(mlb_model* M) {
+    for (StatRec& r : M->pending) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) ms = 0.0f;
+        StatAgg& a = M->agg[r.site + "|" + r.kernel];
+        a.site = r.site; a.kernel = r.kernel;
+        a.launches += 1; a.ms += ms; a.flops += r.flops; a.bytes += r.bytes;
+        M->free_events.push_back(r.e0);
+        M->free_events.push_back(r.e1);
+    }
+    M->pending.clear();
+}
+
+// Algorithmic FLOPs of a contraction: 2 per valid (i, j, k) triple.
+double gemm_flops(const mlb::GemmDesc& g) {
+    double pairs = 0.0;
+    const double M = (double)g.M, N = (double)g.N, K = (double)g.K;
+    if (g.outmask) {            // j <= i, all k
+        const double m = std::min(M, N);
+        pairs = (m * (m + 1) / 2 + (M - m) * N) * K;
+    } else if (g.krange == 1) { // k <= i
+        const double m = std::min(M, K);
+        pairs = (m * (m + 1) / 2 + (M - m) * K) * N;
+    } else if (g.krange == 2) { // k >= i
+        const double m = std::min(M, K);
+        pairs = (m * (m + 1) / 2) * N;
+    } else {
+        pairs = M * N * K;
+    }
+    return 2.0 * pairs * (double)g.batch;
+}
+
+mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
+    mlb::GemmPlan p;
+    p.scratch = M->split;
+    p.scratch_floats = M->split_n;
+    const int64_t ev = stat_begin(M);
+    const int r = mlb::gemm(g, p, M->stream);
+    stat_end(M, ev, site, mlb::gemm_last_kernel(), gemm_flops(g), 0.0);
+    if (r != 0) return fail(MLB_E_DEVICE, "contraction %ldx%ldx%ld failed (%d)", (long)g.M, (long)g.N, (long)g.K, r);
+    return MLB_OK;
+}
+
+#define RUN(site, g)                                 \
+    do {                                             \
+        mlb_status st_ = run_gemm(M, site, (g));     \
+        if (st_ != MLB_OK) return st_;               \
+    } while (0)
+
+// A row or elementwise kernel with its algorithmic HBM bytes.
+#define OP(site, bytes, x)                                                           \
+    do {                                                                             \
+        const int64_t ev_ = stat_begin(M);                                           \
+        const int r_ = (x);                                                          \
+        stat_end(M, ev_, site, site, 0.0, (double)(bytes));                          \
+        if (r_ != 0) return fail(MLB_E_DEVICE, "%s returned %d", #x, r_);            \
+    } while (0)
+
+// Per-head attention contractions on [N, 3d] (q | k | v) and [N, d] rows.
+mlb::GemmDesc head_gemm(const Sizes& s) {
+    mlb::GemmDesc g;
+    g.batch = s.B * s.H;
+    g.H = s.H;
+    return g;
+}
+
+mlb_status forward(mlb_model* M) {
+    const Sizes& s = M->s;
+    hipStream_t st = M->stream;
+    const int64_t N = s.N, d = s.d, F = s.F, T = s.T, H = s.H, hd = s.hd, BH = s.B * s.H;
+    const double f4 = 4.0, tri = (double)BH * (double)T * (double)(T + 1) / 2.0;
+    OP("embed_gather", f4 * 2 * N * d, mlb::gather_rows(M->ids, M->p + M->offE, s.V, d, N, M->h[0], M->err, st));
+    for (int64_t l = 0; l < s.L; ++l) {
+        OP("rmsnorm_fwd", f4 * (2 * N * d + N + d),
+           mlb::rmsnorm_fwd(M->h[l], M->p + M->o_w1[l], N, d, M->cfg.rms_eps, M->xn1[l], M->r1[l], st));
+        RUN("qkv_fwd", lin(N, 3 * d, d, M->xn1[l], d, true, M->p + M->o_qkv[l], d, true, M->qkv[l], 3 * d, 0));
+        OP("rope_fwd", f4 * 4 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+        OP("rope_fwd", f4 * 4 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+        mlb::GemmDesc sg = head_gemm(s);   // S = (q . k) * scale, j <= i
+        sg.M = T; sg.N = T; sg.K = hd; sg.kseg = hd;
+        sg.A = M->qkv[l]; sg.lda = 3 * d; sg.a_kc = true; sg.sAb = T * 3 * d; sg.sAh = hd;
+        sg.B = M->qkv[l] + d; sg.ldb = 3 * d; sg.b_kc = true; sg.sBb = T * 3 * d; sg.sBh = hd;
+        sg.C = M->P[l]; sg.ldc = T; sg.sCb = H * T * T; sg.sCh = T * T;
+        sg.outmask = 1; sg.mode = 2; sg.scale = M->attn_scale;
+        RUN("attn_scores", sg);
+        OP("softmax_fwd", f4 * 2 * tri, mlb::softmax_causal(M->P[l], BH, T, st));
+        mlb::GemmDesc pv = head_gemm(s);   // O = P v over j <= i
+        pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.krange = 1;
+        pv.A = M->P[l]; pv.lda = T; pv.a_kc = true; pv.sAb = H * T * T; pv.sAh = T * T;
+        pv.B = M->qkv[l] + 2 * d; pv.ldb = 3 * d; pv.b_kc = false; pv.sBb = T * 3 * d; pv.sBh = hd;
+        pv.C = M->O[l]; pv.ldc = d; pv.sCb = T * d; pv.sCh = hd;
+        RUN("attn_pv", pv);
+        mlb::GemmDesc wo = lin(N, d, d, M->O[l], d, true, M->p + M->o_wo[l], d, true, M->hmid[l], d, 3);
+        wo.R = M->h[l];                    // hmid = h + O Wo^T
+        RUN("wo_fwd", wo);
+        OP("rmsnorm_fwd", f4 * (2 * N * d + N + d),
+           mlb::rmsnorm_fwd(M->hmid[l], M->p + M->o_w2[l], N, d, M->cfg.rms_eps, M->xn2[l], M->r2[l], st));
+        RUN("gu_fwd", lin(N, 2 * F, d, M->xn2[l], d, true, M->p + M->o_gu[l], d, true, M->gu[l], 2 * F, 0));
+        OP("swiglu_fwd", f4 * 3 * N * F, mlb::swiglu_fwd(M->gu[l], N, F, M->a[l], st));
+        mlb::GemmDesc wd = lin(N, d, F, M->a[l], F, true, M->p + M->o_wd[l], F, true, M->h[l + 1], d, 3);
+        wd.R = M->hmid[l];                 // h' = hmid + a Wd^T
+        RUN("down_fwd", wd);
+    }
+    RUN("head_fwd", lin(N, s.V, d, M->h[s.L], d, true, M->p + M->offOut, d, true, M->logits, s.V, 0));
+    OP("xent", f4 * 2 * N * s.V, mlb::cross_entropy(M->logits, M->tg, N, s.V, M->loss_rows, M->logits, M->err, st));
+    OP("loss_sum", f4 * N, mlb::sum64_scaled(M->loss_rows, N, M->invN, M->loss_dev, st));
+    return MLB_OK;
+}
+
+mlb_status backward(mlb_model* M) {
+    const Sizes& s = M->s;
+    hipStream_t st = M->stream;
+    const int64_t N = s.N, d = s.d, F = s.F, T = s.T, H = s.H, hd = s.hd, BH = s.B * s.H;
+    const double f4 = 4.0, tri = (double)BH * (double)T * (double)(T + 1) / 2.0;
+    const float* dl = M->logits;
+    // head: dh = dl W_out (K = V); W_out gradient = dl^T h_L (K = N), folded into G
+    RUN("head_dx", lin(N, d, s.V, dl, s.V, true, M->p + M->offOut, d, false, M->dh, d, 0));
+    if (s.tied) RUN("head_dw", lin(s.V, d, N, dl, s.V, false, M->h[s.L], d, false, M->gE, d, 0));
+    else RUN("head_dw", lin(s.V, d, N, dl, s.V, false, M->h[s.L], d, false, M->G + M->offOut, d, 1));
+    for (int64_t l = s.L - 1; l >= 0; --l) {
+        // MLP branch
+        RUN("down_dx", lin(N, F, d, M->dh, d, true, M->p + M->o_wd[l], F, false, M->dA, F, 0));
+        RUN("down_dw", lin(d, F, N, M->dh, d, false, M->a[l], F, false, M->G + M->o_wd[l], F, 1));
+        OP("swiglu_bwd", f4 * 5 * N * F, mlb::swiglu_bwd(M->dA, M->gu[l], N, F, M->dgu, st));
+        RUN("gu_dw", lin(2 * F, d, N, M->dgu, 2 * F, false, M->xn2[l], d, false, M->G + M->o_gu[l], d, 1));
+        mlb::GemmDesc x2 = lin(N, d, 2 * F, M->dgu, 2 * F, true, M->p + M->o_gu[l], d, false, M->dxn, d, 0);
+        x2.kseg = F;                       // segments [dg Wg, du Wu]
+        RUN("gu_dx", x2);
+        OP("rmsnorm_dw", f4 * (2 * N * d + N + d),
+           mlb::rmsnorm_bwd_dw(M->dxn, M->hmid[l], M->r2[l], N, d, M->dwpart, M->G + M->o_w2[l], 1, st));
+        OP("rmsnorm_dx", f4 * (4 * N * d + N + d),
+           mlb::rmsnorm_bwd_dx(M->dxn, M->hmid[l], M->p + M->o_w2[l], M->r2[l], N, d, M->dh, 1, st));
+        // attention branch
+        RUN("wo_dx", lin(N, d, d, M->dh, d, true, M->p + M->o_wo[l], d, false, M->dO, d, 0));
+        RUN("wo_dw", lin(d, d, N, M->dh, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
+        OP("attn_rowdot", f4 * (2 * N * d + BH * T), mlb::attn_rowdot(M->dO, M->O[l], s.B, H, T, hd, d, M->Dv, st));
+        mlb::GemmDesc dp = head_gemm(s);   // dP = dO . v, j <= i
+        dp.M = T; dp.N = T; dp.K = hd; dp.kseg = hd; dp.outmask = 1;
+        dp.A = M->dO; dp.lda = d; dp.a_kc = true; dp.sAb = T * d; dp.sAh = hd;
+        dp.B = M->qkv[l] + 2 * d; dp.ldb = 3 * d; dp.b_kc = true; dp.sBb = T * 3 * d; dp.sBh = hd;
+        dp.C = M->dP; dp.ldc = T; dp.sCb = H * T * T; dp.sCh = T * T;
+        RUN("attn_dp", dp);
+        mlb::GemmDesc dv = head_gemm(s);   // dv = P^T dO over i >= j
+        dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.krange = 2;
+        dv.A = M->P[l]; dv.lda = T; dv.a_kc = false; dv.sAb = H * T * T; dv.sAh = T * T;
+        dv.B = M->dO; dv.ldb = d; dv.b_kc = false; dv.sBb = T * d; dv.sBh = hd;
+        dv.C = M->dqkv + 2 * d; dv.ldc = 3 * d; dv.sCb = T * 3 * d; dv.sCh = hd;
+        RUN("attn_dv", dv);
+        OP("softmax_bwd", f4 * 3 * tri, mlb::softmax_bwd(M->P[l], M->dP, M->Dv, BH, T, M->attn_scale, st));
+        mlb::GemmDesc dq = head_gemm(s);   // dq = dS k over j <= i
+        dq.M = T; dq.N = hd; dq.K = T; dq.kseg = T; dq.krange = 1;
+        dq.A = M->dP; dq.lda = T; dq.a_kc = true; dq.sAb = H * T * T; dq.sAh = T * T;
+        dq.B = M->qkv[l] + d; dq.ldb = 3 * d; dq.b_kc = false; dq.sBb = T * 3 * d; dq.sBh = hd;
+        dq.C = M->dqkv; dq.ldc = 3 * d; dq.sCb = T * 3 * d; dq.sCh = hd;
+        RUN("attn_dq", dq);
+        mlb::GemmDesc dk = head_gemm(s);   // dk = dS^T q over i >= j
+        dk.M = T; dk.N = hd; dk.K = T; dk.kseg = T; dk.krange = 2;
+        dk.A = M->dP; dk.lda = T; dk.a_kc = false; dk.sAb = H * T * T; dk.sAh = T * T;
+        dk.B = M->qkv[l]; dk.ldb = 3 * d; dk.b_kc = false; dk.sBb = T * 3 * d; dk.sBh = hd;
+        dk.C = M->dqkv + d; dk.ldc = 3 * d; dk.sCb = T * 3 * d; dk.sCh = hd;
+        RUN("attn_dk", dk);
+        OP("rope_bwd", f4 * 4 * N * d, mlb::rope(M->dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        OP("rope_bwd", f4 * 4 * N * d, mlb::rope(M->dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        RUN("qkv_dw", lin(3 * d, d, N, M->dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1));
+        mlb::GemmDesc x1 = lin(N, d, 3 * d, M->dqkv, 3 * d, true, M->p + M->o_qkv[l], d, false, M->dxn, d, 0);
+        x1.kseg = d;                       // segments [dq Wq, dk Wk, dv Wv]
+        RUN("qkv_dx", x1);
+        OP("rmsnorm_dw", f4 * (2 * N * d + N + d),
+           mlb::rmsnorm_bwd_dw(M->dxn, M->h[l], M->r1[l], N, d, M->dwpart, M->G + M->o_w1[l], 1, st));
+        OP("rmsnorm_dx", f4 * (4 * N * d + N + d),
+           mlb::rmsnorm_bwd_dx(M->dxn, M->h[l], M->p + M->o_w1[l], M->r1[l], N, d, M->dh, 1, st));
+    }
+    // embedding rows in token order (tied: on top of the head gradient, then folded)
+    if (s.tied) {
+        OP("embed_scatter", f4 * 3 * N * d,
+           mlb::embed_scatter(M->ids, M->dh, N, d, s.V, M->gE, M->gE, 0, M->keys, st));
+        OP("embed_fold", f4 * 3 * s.V * d, mlb::add_inplace(M->G + M->offE, M->gE, s.V * d, st));
+    } else {
+        OP("embed_scatter", f4 * 3 * N * d,
+           mlb::embed_scatter(M->ids, M->dh, N, d, s.V, nullptr, M->G + M->offE, 1, M->keys, st));
+    }
+    return MLB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t mlb_param_count(const mlb_config* cfg) {
+    std::string why;
+    if (!cfg_valid(cfg, &why)) return -1;
+    return sizes_of(cfg).P;
+}
+
+mlb_status mlb_workspace_bytes(const mlb_config* cfg, size_t* bytes) {
+    std::string why;
+    if (!bytes) return fail(MLB_E_INVALID_ARG, "bytes is null");
+    if (!cfg_valid(cfg, &why)) return fail(MLB_E_INVALID_ARG, "%s", why.c_str());
+    if (!cfg_supported(cfg, &why)) return fail(MLB_E_UNSUPPORTED, "%s", why.c_str());
+    mlb_model tmp{};
+    tmp.cfg = *cfg;
+    tmp.s = sizes_of(cfg);
+    *bytes = carve(&tmp, nullptr);
+    return MLB_OK;
+}
+
+mlb_status mlb_init(const mlb_config* cfg, const float* init, void* arena, size_t arena_bytes, void* stream,
+                    mlb_model** out) {
+    std::string why;
+    if (!out || !init || !arena) return fail(MLB_E_INVALID_ARG, "null argument");
+    *out = nullptr;
+    if (!cfg_valid(cfg, &why)) return fail(MLB_E_INVALID_ARG, "%s", why.c_str());
+    if (!cfg_supported(cfg, &why)) return fail(MLB_E_UNSUPPORTED, "%s", why.c_str());
+    if ((uintptr_t)arena % ALIGN) return fail(MLB_E_INVALID_ARG, "arena not 256-byte aligned");
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    HIPCHK(hipGetDeviceProperties(&prop, dev));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MLB_E_UNSUPPORTED, "device %s is not gfx950: the profile is certified on gfx950 only",
+                    prop.gcnArchName);
+    mlb_model* M = new mlb_model();
+    M->cfg = *cfg;
+    M->s = sizes_of(cfg);
+    M->stream = static_cast<hipStream_t>(stream);
+    M->device = dev;
+    const size_t need = carve(M, nullptr);
+    if (arena_bytes < need) {
+        delete M;
+        return fail(MLB_E_ARENA_TOO_SMALL, "arena holds %zu bytes, %zu needed", arena_bytes, need);
+    }
+    carve(M, static_cast<char*>(arena));
+    offsets(M);
+    M->attn_scale = (float)(1.0 / std::sqrt((double)M->s.hd));
+    M->invN = 1.0f / (float)M->s.N;
+    if (hipHostMalloc(reinterpret_cast<void**>(&M->host_stage), 64, hipHostMallocDefault) != hipSuccess) {
+        delete M;
+        return fail(MLB_E_DEVICE, "pinned staging buffer");
+    }
+    std::vector<float> c, sn;
+    rope_table_host(M->s.T, M->s.hd, cfg->rope_theta, c, sn);
+    hipStream_t st = M->stream;
+    mlb_status rc = MLB_OK;
+    auto step = [&](hipError_t e, const char* what) {
+        if (rc == MLB_OK && e != hipSuccess) rc = fail(MLB_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    };
+    step(hipMemcpyAsync(M->p, init, (size_t)M->s.P * 4, hipMemcpyHostToDevice, st), "upload params");
+    step(hipMemcpyAsync(M->cosv, c.data(), c.size() * 4, hipMemcpyHostToDevice, st), "upload rope");
+    step(hipMemcpyAsync(M->sinv, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, st), "upload rope");
+    if (rc == MLB_OK) {
+        if (mlb::fill_zero(M->G, M->s.P, st) || mlb::fill_zero(M->m, M->s.P, st) || mlb::fill_zero(M->v, M->s.P, st))
+            rc = fail(MLB_E_DEVICE, "zero fill");
+    }
+    step(hipStreamSynchronize(st), "init sync");
+    if (rc != MLB_OK) {
+        (void)hipHostFree(M->host_stage);
+        delete M;
+        return rc;
+    }
+    M->step = 0;
+    M->have_fwd = false;
+    M->n_accum = 0;
+    *out = M;
+    return MLB_OK;
+}
+
+mlb_status mlb_forward_loss(mlb_model* M, const int32_t* d_inputs, const int32_t* d_targets, float* out_loss) {
+    if (!M || !d_inputs || !d_targets || !out_loss) return fail(MLB_E_INVALID_ARG, "null argument");
+    HIPCHK(hipSetDevice(M->device));
+    M->have_fwd = false;
+    const size_t nb = (size_t)M->s.N * 4;
+    HIPCHK(hipMemcpyAsync(M->ids, d_inputs, nb, hipMemcpyDeviceToDevice, M->stream));
+    HIPCHK(hipMemcpyAsync(M->tg, d_targets, nb, hipMemcpyDeviceToDevice, M->stream));
+    KCHK(mlb::fill_zero(reinterpret_cast<float*>(M->err), 1, M->stream));
+    mlb_status rc = forward(M);
+    if (rc != MLB_OK) return rc;
+    HIPCHK(hipMemcpyAsync(M->host_stage, M->loss_dev, 4, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipMemcpyAsync(M->host_stage + 1, M->err, 4, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    stat_resolve(M);
+    int err;
+    std::memcpy(&err, M->host_stage + 1, 4);
+    if (err) return fail(MLB_E_BAD_TOKEN, "token id outside [0, %u) in %s", M->cfg.vocab,
+                         (err & 1) ? "inputs" : "targets");
+    *out_loss = M->host_stage[0];
+    M->have_fwd = true;
+    return MLB_OK;
+}
+
+mlb_status mlb_backward(mlb_model* M) {
+    if (!M) return fail(MLB_E_INVALID_ARG, "null model");
+    if (!M->have_fwd) return fail(MLB_E_STATE, "backward needs a successful forward of the same micro-batch");
+    HIPCHK(hipSetDevice(M->device));
+    mlb_status rc = backward(M);
+    if (rc != MLB_OK) return rc;
+    M->have_fwd = false;
+    M->n_accum += 1;
+    return MLB_OK;
+}
+
+mlb_status mlb_adamw_step(mlb_model* M, float lr) {
+    if (!M) return fail(MLB_E_INVALID_ARG, "null model");
+    if (M->n_accum < 1) return fail(MLB_E_STATE, "no gradient accumulated since the last step");
+    HIPCHK(hipSetDevice(M->device));
+    const uint64_t t = M->step + 1;
+    const float bc1 = bias_corr(M->cfg.beta1, t), bc2 = bias_corr(M->cfg.beta2, t);
+    OP("adamw", 4.0 * 8 * (double)M->s.P,
+       mlb::adamw(M->p, M->G, M->m, M->v, M->s.P, lr, M->cfg.beta1, M->cfg.beta2, M->cfg.adam_eps,
+                  M->cfg.weight_decay, bc1, bc2, M->stream));
+    M->step = t;
+    M->n_accum = 0;
+    M->have_fwd = false;
+    return MLB_OK;
+}
+
+namespace {
+constexpr size_t HDR = 256;
+
+void put32(uint8_t* p, uint32_t v) { std::memcpy(p, &v, 4); }   // little-endian host
+void put64(uint8_t* p, uint64_t v) { std::memcpy(p, &v, 8); }
+
+void header(const mlb_config& c, uint64_t step, uint64_t n, const uint8_t dp[32], const uint8_t dm[32],
+            const uint8_t dv[32], uint8_t* h) {
+    std::memset(h, 0, HDR);
+    std::memcpy(h, "MLBCKPT1", 8);
+    put32(h + 8, 1u);
+    put32(h + 12, MLB_PROFILE_VERSION);
+    const uint32_t ci[9] = {c.vocab, c.d_model, c.n_layers, c.n_heads, c.head_dim, c.ffn_hidden, c.tied, c.batch,
+                            c.seq_len};
+    std::memcpy(h + 16, ci, 36);
+    const float cf[6] = {c.rope_theta, c.rms_eps, c.beta1, c.beta2, c.adam_eps, c.weight_decay};
+    std::memcpy(h + 52, cf, 24);
+    put64(h + 80, step);
+    put64(h + 88, n);
+    std::memcpy(h + 96, dp, 32);
+    std::memcpy(h + 128, dm, 32);
+    std::memcpy(h + 160, dv, 32);
+    sha256_bytes(h, 192, h + 192);
+}
+}  // namespace
+
+mlb_status mlb_save(const mlb_model* M, void* buf, size_t cap, size_t* len) {
+    if (!M || !len) return fail(MLB_E_INVALID_ARG, "null argument");
+    const size_t nb = (size_t)M->s.P * 4, total = HDR + 3 * nb;
+    *len = total;
+    if (!buf) return MLB_OK;
+    if (M->n_accum != 0) return fail(MLB_E_STATE, "save with pending accumulated gradients");
+    if (cap < total) return fail(MLB_E_IO, "buffer holds %zu bytes, %zu needed", cap, total);
+    HIPCHK(hipSetDevice(M->device));
+    uint8_t* b = static_cast<uint8_t*>(buf);
+    HIPCHK(hipStreamSynchronize(M->stream));
+    HIPCHK(hipMemcpy(b + HDR, M->p, nb, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(b + HDR + nb, M->m, nb, hipMemcpyDeviceToHost));
+    HIPCHK(hipMemcpy(b + HDR + 2 * nb, M->v, nb, hipMemcpyDeviceToHost));
+    uint8_t dp[32], dm[32], dv[32];
+    sha256_bytes(b + HDR, nb, dp);
+    sha256_bytes(b + HDR + nb, nb, dm);
+    sha256_bytes(b + HDR + 2 * nb, nb, dv);
+    header(M->cfg, M->step, (uint64_t)M->s.P, dp, dm, dv, b);
+    return MLB_OK;
+}
+
+mlb_status mlb_load(mlb_model* M, const void* buf, size_t len) {
+    if (!M || !buf) return fail(MLB_E_INVALID_ARG, "null argument");
+    const uint8_t* b = static_cast<const uint8_t*>(buf);
+    if (len < HDR) return fail(MLB_E_CORRUPT, "truncated header");
+    if (std::memcmp(b, "MLBCKPT1", 8) != 0) return fail(MLB_E_PROFILE_MISMATCH, "not an MLBC checkpoint");
+    uint32_t fmt, prof;
+    std::memcpy(&fmt, b + 8, 4);
+    std::memcpy(&prof, b + 12, 4);
+    if (fmt != 1u || prof != MLB_PROFILE_VERSION)
+        return fail(MLB_E_PROFILE_MISMATCH, "format %u profile %u (expected 1, %u)", fmt, prof, MLB_PROFILE_VERSION);
+    uint8_t hd[32];
+    sha256_bytes(b, 192, hd);
+    if (std::memcmp(hd, b + 192, 32) != 0) return fail(MLB_E_CORRUPT, "header digest mismatch");
+    uint8_t zeros[32] = {0};
+    if (std::memcmp(b + 224, zeros, 32) != 0 || b[76] | b[77] | b[78] | b[79])
+        return fail(MLB_E_CORRUPT, "header padding not zero");
+    const mlb_config& c = M->cfg;
+    const uint32_t ci[9] = {c.vocab, c.d_model, c.n_layers, c.n_heads, c.head_dim, c.ffn_hidden, c.tied, c.batch,
+                            c.seq_len};
+    const float cf[6] = {c.rope_theta, c.rms_eps, c.beta1, c.beta2, c.adam_eps, c.weight_decay};
+    if (std::memcmp(b + 16, ci, 36) != 0 || std::memcmp(b + 52, cf, 24) != 0)
+        return fail(MLB_E_CONFIG_MISMATCH, "checkpoint config differs from the model's");
+    uint64_t step, n;
+    std::memcpy(&step, b + 80, 8);
+    std::memcpy(&n, b + 88, 8);
+    const size_t nb = (size_t)M->s.P * 4;
+    if (n != (uint64_t)M->s.P || len != HDR + 3 * nb) return fail(MLB_E_CORRUPT, "size mismatch");
+    uint8_t d3[3][32];
+    for (int i = 0; i < 3; ++i) {
+        sha256_bytes(b + HDR + i * nb, nb, d3[i]);
+        if (std::memcmp(d3[i], b + 96 + 32 * i, 32) != 0) return fail(MLB_E_CORRUPT, "array %d digest mismatch", i);
+    }
+    HIPCHK(hipSetDevice(M->device));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    HIPCHK(hipMemcpy(M->p, b + HDR, nb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(M->m, b + HDR + nb, nb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(M->v, b + HDR + 2 * nb, nb, hipMemcpyHostToDevice));
+    KCHK(mlb::fill_zero(M->G, M->s.P, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    M->step = step;
+    M->n_accum = 0;
+    M->have_fwd = false;
+    return MLB_OK;
+}
+
+mlb_status mlb_read(const mlb_model* M, mlb_which w, void* dst, size_t bytes) {
+    if (!M || !dst) return fail(MLB_E_INVALID_ARG, "null argument");
+    const size_t nb = (size_t)M->s.P * 4;
+    if (bytes < nb) return fail(MLB_E_IO, "buffer holds %zu bytes, %zu needed", bytes, nb);
+    const float* src = w == MLB_PARAMS ? M->p : w == MLB_GRAD ? M->G : w == MLB_ADAM_M ? M->m : w == MLB_ADAM_V ? M->v
+                                                                                                                 : nullptr;
+    if (!src) return fail(MLB_E_INVALID_ARG, "unknown array %d", (int)w);
+    HIPCHK(hipSetDevice(M->device));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    HIPCHK(hipMemcpy(dst, src, nb, hipMemcpyDeviceToHost));
+    return MLB_OK;
+}
+
+mlb_status mlb_read_stage(const mlb_model* M, int stage, int layer, void* dst, size_t bytes, size_t* count) {
+    if (!M || !count) return fail(MLB_E_INVALID_ARG, "null argument");
+    const Sizes& s = M->s;
+    if (layer < 0 || layer >= s.L) return fail(MLB_E_INVALID_ARG, "layer %d out of range", layer);
+    const float* src = nullptr;
+    int64_t n = 0;
+    switch (stage) {
+        case 0: src = M->h[layer]; n = s.N * s.d; break;
+        case 1: src = M->xn1[layer]; n = s.N * s.d; break;
+        case 2: src = M->r1[layer]; n = s.N; break;
+        case 3: src = M->qkv[layer]; n = s.N * 3 * s.d; break;
+        case 4: src = M->P[layer]; n = s.B * s.H * s.T * s.T; break;
+        case 5: src = M->O[layer]; n = s.N * s.d; break;
+        case 6: src = M->hmid[layer]; n = s.N * s.d; break;
+        case 7: src = M->xn2[layer]; n = s.N * s.d; break;
+        case 8: src = M->r2[layer]; n = s.N; break;
+        case 9: src = M->gu[layer]; n = s.N * 2 * s.F; break;
+        case 10: src = M->a[layer]; n = s.N * s.F; break;
+        case 11: src = M->h[s.L]; n = s.N * s.d; break;
+        case 12: src = M->logits; n = s.N * s.V; break;
+        case 13: src = M->loss_rows; n = s.N; break;
+        default: return fail(MLB_E_INVALID_ARG, "unknown stage %d", stage);
+    }
+    *count = (size_t)n;
+    if (!dst) return MLB_OK;
+    if (bytes < (size_t)n * 4) return fail(MLB_E_IO, "buffer too small");
+    HIPCHK(hipSetDevice(M->device));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    HIPCHK(hipMemcpy(dst, src, (size_t)n * 4, hipMemcpyDeviceToHost));
+    return MLB_OK;
+}
+
+uint64_t mlb_step(const mlb_model* M) { return M ? M->step : 0; }
+
+mlb_status mlb_destroy(mlb_model* M) {
+    if (!M) return MLB_OK;
+    (void)hipSetDevice(M->device);
+    (void)hipStreamSynchronize(M->stream);
+    stat_resolve(M);
+    for (hipEvent_t e : M->free_events) (void)hipEventDestroy(e);
+    (void)hipHostFree(M->host_stage);
+    delete M;
+    return MLB_OK;
+}
+
+mlb_status mlb_stats_enable(mlb_model* M, int on) {
+    if (!M) return fail(MLB_E_INVALID_ARG, "null model");
+    HIPCHK(hipSetDevice(M->device));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    stat_resolve(M);
+    M->agg.clear();
+    M->stats_on = on != 0;
+    return MLB_OK;
+}
+
+mlb_status mlb_stats_read(mlb_model* M, mlb_stat* out, int cap, int* n) {
+    if (!M || !n) return fail(MLB_E_INVALID_ARG, "null argument");
+    HIPCHK(hipSetDevice(M->device));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    stat_resolve(M);
+    *n = (int)M->agg.size();
+    int i = 0;
+    for (const auto& kv : M->agg) {
+        if (!out || i >= cap) break;
+        mlb_stat& o = out[i++];
+        std::memset(&o, 0, sizeof o);
+        std::snprintf(o.site, sizeof o.site, "%s", kv.second.site.c_str());
+        std::snprintf(o.kernel, sizeof o.kernel, "%s", kv.second.kernel.c_str());
+        o.launches = kv.second.launches;
+        o.ms = kv.second.ms;
+        o.flops = kv.second.flops;
+        o.bytes = kv.second.bytes;
+    }
+    return MLB_OK;
+}
+
+const char* mlb_status_name(mlb_status s) {
+    switch (s) {
+        case MLB_OK: return "MLB_OK";
+        case MLB_E_INVALID_ARG: return "MLB_E_INVALID_ARG";
+        case MLB_E_UNSUPPORTED: return "MLB_E_UNSUPPORTED";
+        case MLB_E_DEVICE: return "MLB_E_DEVICE";
+        case MLB_E_ARENA_TOO_SMALL: return "MLB_E_ARENA_TOO_SMALL";
+        case MLB_E_BAD_TOKEN: return "MLB_E_BAD_TOKEN";
+        case MLB_E_STATE: return "MLB_E_STATE";
+        case MLB_E_CORRUPT: return "MLB_E_CORRUPT";
+        case MLB_E_PROFILE_MISMATCH: return "MLB_E_PROFILE_MISMATCH";
+        case MLB_E_CONFIG_MISMATCH: return "MLB_E_CONFIG_MISMATCH";
+        case MLB_E_IO: return "MLB_E_IO";
+        default: return "MLB_E_UNKNOWN";
+    }
+}
+
+const char* mlb_last_error_message(void) { return g_msg; }
+uint32_t mlb_profile_version(void) { return MLB_PROFILE_VERSION; }
+
+// ------------------------------------------------------------- primitives
+mlb_status mlb_prim_gemm(int64_t M, int64_t N, int64_t K, int64_t kseg, const float* A, int64_t lda, int a_kc,
+                         const float* B, int64_t ldb, int b_kc, float* C, int64_t ldc, int krange, int outmask,
+                         int mode, float scale, int64_t batch, int64_t heads, int64_t sAb, int64_t sAh, int64_t sBb,
+                         int64_t sBh, int64_t sCb, int64_t sCh, int tile, int split, int simple, void* ws,
+                         size_t ws_bytes, void* stream) {
+    if (mode < 0 || mode > 2) return fail(MLB_E_INVALID_ARG, "mode %d", mode);
+    mlb::GemmDesc g;
+    g.M = M; g.N = N; g.K = K; g.kseg = kseg > 0 ? kseg : K;
+    g.A = A; g.lda = lda; g.a_kc = a_kc != 0; g.B = B; g.ldb = ldb; g.b_kc = b_kc != 0; g.C = C; g.ldc = ldc;
+    g.krange = krange; g.outmask = outmask; g.mode = mode; g.scale = scale;
+    g.batch = batch; g.H = heads; g.sAb = sAb; g.sAh = sAh; g.sBb = sBb; g.sBh = sBh; g.sCb = sCb; g.sCh = sCh;
+    if (tile < -1 || tile > 1) return fail(MLB_E_INVALID_ARG, "tile %d", tile);
+    mlb::GemmPlan p;
+    p.tile = tile; p.split = split; p.simple = simple;
+    p.scratch = static_cast<float*>(ws);
+    p.scratch_floats = (int64_t)(ws_bytes / 4);
+    if (split == 1 && mlb::gemm_split_scratch(g, p) > p.scratch_floats)
+        return fail(MLB_E_ARENA_TOO_SMALL, "split needs %ld floats", (long)mlb::gemm_split_scratch(g, p));
+    const int r = mlb::gemm(g, p, static_cast<hipStream_t>(stream));
+    if (r == -1) return fail(MLB_E_INVALID_ARG, "invalid contraction description");
+    if (r != 0) return fail(MLB_E_DEVICE, "contraction launch failed (%d)", r);
+    return MLB_OK;
+}
+
+mlb_status mlb_prim_rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float eps, float* y, float* r,
+                                void* stream) {
+    if (!x || !w || !y || !r) return fail(MLB_E_INVALID_ARG, "null argument");
+    return mlb::rmsnorm_fwd(x, w, rows, d, eps, y, r, static_cast<hipStream_t>(stream)) == 0
+               ? MLB_OK
+               : fail(MLB_E_INVALID_ARG, "rmsnorm_fwd");
+}
+
+mlb_status mlb_prim_rmsnorm_bwd(const float* dy, const float* x, const float* w, const float* r, int64_t rows,
+                                int64_t d, float* dx, float* dw, void* ws, size_t ws_bytes, void* stream) {
+    if (!dy || !x || !w || !r || !dx || !dw) return fail(MLB_E_INVALID_ARG, "null argument");
+    const size_t need = (size_t)((rows + KCH - 1) / KCH) * (size_t)d * 4;
+    if (ws_bytes < need || (!ws && need)) return fail(MLB_E_ARENA_TOO_SMALL, "rmsnorm_bwd needs %zu bytes", need);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (mlb::rmsnorm_bwd_dx(dy, x, w, r, rows, d, dx, 0, st) ||
+        mlb::rmsnorm_bwd_dw(dy, x, r, rows, d, static_cast<float*>(ws), dw, 0, st))
+        return fail(MLB_E_INVALID_ARG, "rmsnorm_bwd");
+    return MLB_OK;
+}
+
+mlb_status mlb_prim_rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, float theta, int backward,
+                         void* stream) {
+    if (!x || hd % 2 || T <= 0) return fail(MLB_E_INVALID_ARG, "rope arguments");
+    std::vector<float> c, sn;
+    rope_table_host(T, hd, theta, c, sn);
+    float* tab = nullptr;
+    HIPCHK(hipMalloc(reinterpret_cast<void**>(&tab), c.size() * 8));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    HIPCHK(hipMemcpyAsync(tab, c.data(), c.size() * 4, hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(tab + c.size(), sn.data(), c.size() * 4, hipMemcpyHostToDevice, st));
+    const int r = mlb::rope(x, B, T, H, hd, ld, tab, tab + c.size(), backward, st);
+    HIPCHK(hipStreamSynchronize(st));
+    HIPCHK(hipFree(tab));
+    return r == 0 ? MLB_OK : fail(MLB_E_INVALID_ARG, "rope");
+}
+
+mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, const float* k,
+                                  const float* v, int64_t ld, float* P, float* O, int64_t ldo, void* stream) {
+    if (!q || !k || !v || !P || !O || B <= 0 || H <= 0 || T <= 0 || hd <= 0) return fail(MLB_E_INVALID_ARG, "attention");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    mlb::GemmPlan plan;
+    mlb::GemmDesc sg;
+    sg.batch = B * H; sg.H = H;
+    sg.M = T; sg.N = T; sg.K = hd; sg.kseg = hd;
+    sg.A = q; sg.lda = ld; sg.a_kc = true; sg.sAb = T * ld; sg.sAh = hd;
+    sg.B = k; sg.ldb = ld; sg.b_kc = true; sg.sBb = T * ld; sg.sBh = hd;
+    sg.C = P; sg.ldc = T; sg.sCb = H * T * T; sg.sCh = T * T;
+    sg.outmask = 1; sg.mode = 2; sg.scale = (float)(1.0 / std::sqrt((double)hd));
+    if (mlb::gemm(sg, plan, st)) return fail(MLB_E_DEVICE, "scores");
+    if (mlb::softmax_causal(P, B * H, T, st)) return fail(MLB_E_DEVICE, "softmax");
+    mlb::GemmDesc pv;
+    pv.batch = B * H; pv.H = H;
+    pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.krange = 1;
+    pv.A = P; pv.lda = T; pv.a_kc = true; pv.sAb = H * T * T; pv.sAh = T * T;
+    pv.B = v; pv.ldb = ld; pv.b_kc = false; pv.sBb = T * ld; pv.sBh = hd;
+    pv.C = O; pv.ldc = ldo; pv.sCb = T * ldo; pv.sCh = hd;
+    if (mlb::gemm(pv, plan, st)) return fail(MLB_E_DEVICE, "PV");
+    return MLB_OK;
+}
+
+mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, const float* k,
+                                  const float* v, int64_t ld, const float* P, const float* O, const float* dO,
+                                  int64_t ldo, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    if (!q || !k || !v || !P || !O || !dO || !dq || !dk || !dv || B <= 0 || H <= 0 || T <= 0 || hd <= 0)
+        return fail(MLB_E_INVALID_ARG, "attention_bwd");
+    const size_t need = (size_t)(B * H * T * T + B * H * T) * 4;
+    if (!ws || ws_bytes < need) return fail(MLB_E_ARENA_TOO_SMALL, "attention_bwd needs %zu bytes", need);
+    float* dP = static_cast<float*>(ws);
+    float* D = dP + B * H * T * T;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    mlb::GemmPlan plan;
+    const float scale = (float)(1.0 / std::sqrt((double)hd));
+    if (mlb::attn_rowdot(dO, O, B, H, T, hd, ldo, D, st)) return fail(MLB_E_DEVICE, "rowdot");
+    mlb::GemmDesc g;
+    g.batch = B * H; g.H = H;
+    g.M = T; g.N = T; g.K = hd; g.kseg = hd; g.outmask = 1;
+    g.A = dO; g.lda = ldo; g.a_kc = true; g.sAb = T * ldo; g.sAh = hd;
+    g.B = v; g.ldb = ld; g.b_kc = true; g.sBb = T * ld; g.sBh = hd;
+    g.C = dP; g.ldc = T; g.sCb = H * T * T; g.sCh = T * T;
+    if (mlb::gemm(g, plan, st)) return fail(MLB_E_DEVICE, "dP");
+    mlb::GemmDesc gv;
+    gv.batch = B * H; gv.H = H;
+    gv.M = T; gv.N = hd; gv.K = T; gv.kseg = T; gv.krange = 2;
+    gv.A = P; gv.lda = T; gv.a_kc = false; gv.sAb = H * T * T; gv.sAh = T * T;
+    gv.B = dO; gv.ldb = ldo; gv.b_kc = false; gv.sBb = T * ldo; gv.sBh = hd;
+    gv.C = dv; gv.ldc = ld; gv.sCb = T * ld; gv.sCh = hd;
+    if (mlb::gemm(gv, plan, st)) return fail(MLB_E_DEVICE, "dv");
+    if (mlb::softmax_bwd(P, dP, D, B * H, T, scale, st)) return fail(MLB_E_DEVICE, "softmax_bwd");
+    mlb::GemmDesc gq;
+    gq.batch = B * H; gq.H = H;
+    gq.M = T; gq.N = hd; gq.K = T; gq.kseg = T; gq.krange = 1;
+    gq.A = dP; gq.lda = T; gq.a_kc = true; gq.sAb = H * T * T; gq.sAh = T * T;
+    gq.B = k; gq.ldb = ld; gq.b_kc = false; gq.sBb = T * ld; gq.sBh = hd;
+    gq.C = dq; gq.ldc = ld; gq.sCb = T * ld; gq.sCh = hd;
+    if (mlb::gemm(gq, plan, st)) return fail(MLB_E_DEVICE, "dq");
+    mlb::GemmDesc gk;
+    gk.batch = B * H; gk.H = H;
+    gk.M = T; gk.N = hd; gk.K = T; gk.kseg = T; gk.krange = 2;
+    gk.A = dP; gk.lda = T; gk.a_kc = false; gk.sAb = H * T * T; gk.sAh = T * T;
+    gk.B = q; gk.ldb = ld; gk.b_kc = false; gk.sBb = T * ld; gk.sBh = hd;
+    gk.C = dk; gk.ldc = ld; gk.sCb = T * ld; gk.sCh = hd;
+    if (mlb::gemm(gk, plan, st)) return fail(MLB_E_DEVICE, "dk");
+    return MLB_OK;
+}
+
+mlb_status mlb_prim_swiglu_fwd(const float* gu, int64_t rows, int64_t F, float* a, void* stream) {
+    if (!gu || !a) return fail(MLB_E_INVALID_ARG, "null argument");
+    return mlb::swiglu_fwd(gu, rows, F, a, static_cast<hipStream_t>(stream)) == 0 ? MLB_OK
+                                                                                   : fail(MLB_E_DEVICE, "swiglu_fwd");
+}
+
+mlb_status mlb_prim_swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float* dgu, void* stream) {
+    if (!dA || !gu || !dgu) return fail(MLB_E_INVALID_ARG, "null argument");
+    return mlb::swiglu_bwd(dA, gu, rows, F, dgu, static_cast<hipStream_t>(stream)) == 0
+               ? MLB_OK
+               : fail(MLB_E_DEVICE, "swiglu_bwd");
+}
+
+mlb_status mlb_prim_cross_entropy(const float* logits, const int32_t* targets, int64_t N, int64_t V, float* loss_rows,
+                                  float* dl, float* loss_dev, void* stream) {
+    if (!logits || !targets || !loss_rows || !dl || !loss_dev) return fail(MLB_E_INVALID_ARG, "null argument");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int* err = nullptr;
+    HIPCHK(hipMalloc(reinterpret_cast<void**>(&err), 4));
+    HIPCHK(hipMemsetAsync(err, 0, 4, st));
+    const int r = mlb::cross_entropy(logits, targets, N, V, loss_rows, dl, err, st);
+    const int r2 = r == 0 ? mlb::sum64_scaled(loss_rows, N, 1.0f / (float)N, loss_dev, st) : r;
+    int herr = 0;
+    HIPCHK(hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, st));
+    HIPCHK(hipStreamSynchronize(st));
+    HIPCHK(hipFree(err));
+    if (r || r2) return fail(MLB_E_INVALID_ARG, "cross_entropy");
+    if (herr) return fail(MLB_E_BAD_TOKEN, "target outside [0, %ld)", (long)V);
+    return MLB_OK;
+}
+
+mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, float* dE,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    if (!ids || !dh || !dE) return fail(MLB_E_INVALID_ARG, "null argument");
+    if (N > MAX_TOKENS) return fail(MLB_E_UNSUPPORTED, "more than 8192 positions");
+    if (!ws || ws_bytes < (size_t)2 * MAX_TOKENS * 8) return fail(MLB_E_ARENA_TOO_SMALL, "scatter needs 131072 bytes");
+    const int r = mlb::embed_scatter(ids, dh, N, d, V, dE, dE, 0, static_cast<uint64_t*>(ws),
+                                     static_cast<hipStream_t>(stream));
+    return r == 0 ? MLB_OK : fail(MLB_E_INVALID_ARG, "embed_scatter (%d)", r);
+}
+
+mlb_status mlb_prim_adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2,
+                          float eps, float wd, int64_t t, void* stream) {
+    if (!p || !g || !m || !v || t < 1) return fail(MLB_E_INVALID_ARG, "adamw arguments");
+    const int r = mlb::adamw(p, g, m, v, n, lr, beta1, beta2, eps, wd, bias_corr(beta1, (uint64_t)t),
+                             bias_corr(beta2, (uint64_t)t), static_cast<hipStream_t>(stream));
+    return r == 0 ? MLB_OK : fail(MLB_E_DEVICE, "adamw");
+}
+
+mlb_status mlb_prim_unary(const float* x, float* y, int64_t n, int which, void* stream) {
+    if (!x || !y) return fail(MLB_E_INVALID_ARG, "null argument");
+    return mlb::exp_array(x, y, n, which, static_cast<hipStream_t>(stream)) == 0 ? MLB_OK
+                                                                                  : fail(MLB_E_INVALID_ARG, "unary");
+}
+
+mlb_status mlb_diag_mfma(int variant, const float* A, const float* B, const float* C, float* D, int64_t nwaves,
+                         void* stream) {
+    if (!A || !B || !C || !D) return fail(MLB_E_INVALID_ARG, "null argument");
+    return mlb::mfma_probe(variant, A, B, C, D, nwaves, static_cast<hipStream_t>(stream)) == 0
+               ? MLB_OK
+               : fail(MLB_E_INVALID_ARG, "variant %d", variant);
+}
+
+}  // extern "C"

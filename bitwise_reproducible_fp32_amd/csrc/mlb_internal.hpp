@@ -1,0 +1,96 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlb {
+
+// One G1024 contraction (the profile's only matrix-product rule):
+//   t(i,j) = sum_k A(i,k) B(k,j)
+// The K range is split into segments of length kseg; each segment is cut into
+// chunks at multiples of 1024 of its local index; krange 1 keeps k <= i and
+// krange 2 keeps k >= i; every chunk is an fma chain from +0 in ascending k;
+// the non-empty chunks are added left to right. An empty contraction is +0.
+// Epilogue: mode 0 C = t, mode 1 C = C + t, mode 2 C = t * scale, mode 3
+// C = R + t (R a separate residual input with the C layout); outmask writes
+// only j <= i.
+// Layouts: a_kc means A(i,k) = A[i*lda + k] (k contiguous), otherwise
+// A(i,k) = A[k*lda + i]. b_kc means B(k,j) = B[j*ldb + k], otherwise
+// B(k,j) = B[k*ldb + j]. C(i,j) = C[i*ldc + j].
+// Batches: z = zb*H + zh adds zb*s?b + zh*s?h to each base pointer.
+struct GemmDesc {
+    int64_t M = 0, N = 0, K = 0, kseg = 0;
+    const float* A = nullptr; int64_t lda = 0; bool a_kc = true;
+    const float* B = nullptr; int64_t ldb = 0; bool b_kc = true;
+    float* C = nullptr; int64_t ldc = 0;
+    const float* R = nullptr;
+    int64_t batch = 1, H = 1;
+    int64_t sAb = 0, sAh = 0, sBb = 0, sBh = 0, sCb = 0, sCh = 0;
+    int krange = 0, outmask = 0, mode = 0;
+    float scale = 1.0f;
+};
+
+// Host-side launch options. They never change a result bit: the split and
+// tile choices only change which workgroup computes which chunk.
+struct GemmPlan {
+    int tile = -1;            // -1 auto, else a tile configuration index
+    int split = -1;           // -1 auto, 0 never split K into per-chunk partials, 1 split
+    float* scratch = nullptr; // split partial buffer (floats)
+    int64_t scratch_floats = 0;
+    int simple = 0;           // 1: use the one-thread-per-output reference kernel
+};
+
+// Floats of scratch the split path needs for d (0 when it would not split).
+int64_t gemm_split_scratch(const GemmDesc& d, const GemmPlan& p);
+// Returns 0, or a negative value when the description is invalid or unsupported.
+int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s);
+// Name of the contraction kernel the last gemm() call on this thread launched
+// (the split path also launches k_fold).
+const char* gemm_last_kernel();
+
+// Row and elementwise kernels (mlb_ops.hip). All return 0 or a negative value
+// on invalid sizes; they launch on stream s and never synchronise.
+int gather_rows(const int32_t* ids, const float* table, int64_t V, int64_t d, int64_t N, float* out,
+                int* err, hipStream_t s);
+int rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float eps, float* y, float* r,
+                hipStream_t s);
+// dx = rmsnorm backward; written as out = out + dx when accumulate, else out = dx.
+int rmsnorm_bwd_dx(const float* dy, const float* x, const float* w, const float* r, int64_t rows,
+                   int64_t d, float* out, int accumulate, hipStream_t s);
+// Gain gradient: per column the contraction over rows of dy * (x * r), chunks of
+// 1024 rows. part must hold ceil(rows/1024)*d floats. mode 0 dw = t, 1 dw = dw + t.
+int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows, int64_t d, float* part,
+                   float* dw, int mode, hipStream_t s);
+int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, const float* cosv,
+         const float* sinv, int backward, hipStream_t s);
+// In-place causal softmax of rows i of [nbh, T, T] over j <= i.
+int softmax_causal(float* P, int64_t nbh, int64_t T, hipStream_t s);
+// D[z*T + i] = DOT64 over hd of dO and O rows (head layout as q).
+int attn_rowdot(const float* dO, const float* O, int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
+                float* D, hipStream_t s);
+// dS = (P * (dP - D_i)) * scale in place over dP, j <= i.
+int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t T, float scale,
+                hipStream_t s);
+int swiglu_fwd(const float* gu, int64_t rows, int64_t F, float* a, hipStream_t s);
+int swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float* dgu, hipStream_t s);
+// Cross-entropy rows: loss_rows written, dl written (may alias logits).
+int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, float* loss_rows,
+                  float* dl, int* err, hipStream_t s);
+// out[0] = SUM64(v[0..n)) * mul.
+int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s);
+// Embedding-gradient scatter. For every row v that appears in ids, in order of
+// increasing position n: acc = init(v); acc = acc + dh[n]; then
+// dst[v] = acc (mode 0) or dst[v] = dst[v] + acc (mode 1). init(v) is +0 when
+// src_init is null, else src_init[v]. keys must hold 2*N uint64 values.
+int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V,
+                  const float* src_init, float* dst, int mode, uint64_t* keys, hipStream_t s);
+// out = out + x elementwise (n floats).
+int add_inplace(float* out, const float* x, int64_t n, hipStream_t s);
+int adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float b1, float b2, float eps,
+          float wd, float bc1, float bc2, hipStream_t s);
+int exp_array(const float* x, float* y, int64_t n, int which, hipStream_t s);
+int fill_zero(float* x, int64_t n, hipStream_t s);
+int mfma_probe(int variant, const float* A, const float* B, const float* C, float* D, int64_t nwaves,
+               hipStream_t s);
+
+}  // namespace mlb

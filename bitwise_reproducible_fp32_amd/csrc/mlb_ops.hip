@@ -1,0 +1,521 @@
+// Row, elementwise and data-movement kernels of the training step.
+//
+// Each kernel follows one rule of the MLB-P1 profile (restated next to it);
+// the reductions use the W64 lane assignment (element i to lane i mod 64,
+// ascending, then the l <- l+s tree), which one wavefront realises directly.
+// All of these kernels are bound by HBM bandwidth, so they read each input
+// once or a few times with coalesced 64-lane accesses; none uses atomics on
+// floating-point data.
+#include "mlb_device.hpp"
+#include "mlb_internal.hpp"
+
+namespace mlb {
+namespace {
+
+constexpr int64_t KC = 1024;
+
+inline unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+// Embedding lookup: an exact copy of table row ids[n]. An id outside [0, V)
+// writes zeros and raises *err (no out-of-range read).
+__global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ ids, const float* __restrict__ tab,
+                                                int64_t V, int64_t d, int64_t N, float* __restrict__ out,
+                                                int* err) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= N * d) return;
+    const int64_t n = idx / d, c = idx % d;
+    const int32_t id = ids[n];
+    if (id < 0 || id >= V) {
+        out[idx] = 0.0f;
+        if (c == 0) atomicOr(err, 1);
+        return;
+    }
+    out[idx] = tab[(int64_t)id * d + c];
+}
+
+// RMSNorm forward, one wavefront per row:
+// ss = DOT64(x, x); r = 1 / sqrt(ss / d + eps); y = (x * r) * w.
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x, const float* __restrict__ w,
+                                                     int64_t rows, int64_t d, float eps, float* __restrict__ y,
+                                                     float* __restrict__ r) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float* xr = x + row * d;
+    float acc = 0.0f;
+    for (int64_t c = lane; c < d; c += 64) acc = __builtin_fmaf(xr[c], xr[c], acc);
+    const float ss = wave_tree_sum(acc);
+    const float ms = ss / (float)d;
+    const float rr = 1.0f / __builtin_sqrtf(ms + eps);
+    if (lane == 0) r[row] = rr;
+    float* yr = y + row * d;
+    for (int64_t c = lane; c < d; c += 64) yr[c] = (xr[c] * rr) * w[c];
+}
+
+// RMSNorm backward (input gradient), one wavefront per row:
+// xh = x * r; gw = dy * w; c = DOT64(gw, xh) / d; dx = r * (gw - xh * c).
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict__ dy, const float* __restrict__ x,
+                                                        const float* __restrict__ w, const float* __restrict__ r,
+                                                        int64_t rows, int64_t d, float* out, int accumulate) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float rr = r[row];
+    const float* xr = x + row * d;
+    const float* dr = dy + row * d;
+    float acc = 0.0f;
+    for (int64_t c = lane; c < d; c += 64) {
+        const float xh = xr[c] * rr;
+        const float gw = dr[c] * w[c];
+        acc = __builtin_fmaf(gw, xh, acc);
+    }
+    const float cc = wave_tree_sum(acc) / (float)d;
+    float* o = out + row * d;
+    for (int64_t c = lane; c < d; c += 64) {
+        const float xh = xr[c] * rr;
+        const float gw = dr[c] * w[c];
+        const float dx = rr * (gw - (xh * cc));
+        o[c] = accumulate ? o[c] + dx : dx;
+    }
+}
+
+// Gain gradient partials: part[ch][c] = fma chain over rows n of chunk ch
+// (1024 rows) of dy[n,c] * (x[n,c] * r[n]), from +0 in ascending n.
+__global__ __launch_bounds__(256) void k_rmsnorm_dw_part(const float* __restrict__ dy, const float* __restrict__ x,
+                                                         const float* __restrict__ r, int64_t rows, int64_t d,
+                                                         float* __restrict__ part) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t ch = blockIdx.y;
+    if (c >= d) return;
+    const int64_t n0 = ch * KC, n1 = (n0 + KC < rows) ? n0 + KC : rows;
+    float acc = 0.0f;
+    for (int64_t n = n0; n < n1; ++n) acc = __builtin_fmaf(dy[n * d + c], x[n * d + c] * r[n], acc);
+    part[ch * d + c] = acc;
+}
+
+// Left fold of per-chunk column partials, then dw = t (mode 0) or dw + t (mode 1).
+__global__ __launch_bounds__(256) void k_fold_cols(const float* __restrict__ part, int64_t nch, int64_t d,
+                                                   float* dw, int mode) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= d) return;
+    float t = part[c];
+    for (int64_t ch = 1; ch < nch; ++ch) t = t + part[ch * d + c];
+    dw[c] = mode ? dw[c] + t : t;
+}
+
+// Rotary embedding, half-split pairing (element i with i + hd/2) at position
+// t = n mod T, table values cos/sin[t][i].
+__global__ __launch_bounds__(256) void k_rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld,
+                                              const float* __restrict__ cosv, const float* __restrict__ sinv,
+                                              int backward) {
+    const int64_t h2 = hd / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= B * T * H * h2) return;
+    const int64_t i = idx % h2, h = (idx / h2) % H, n = idx / (h2 * H);
+    const int64_t t = n % T;
+    float* row = x + n * ld + h * hd;
+    const float c = cosv[t * h2 + i], s = sinv[t * h2 + i];
+    const float x0 = row[i], x1 = row[i + h2];
+    if (!backward) {
+        row[i] = (x0 * c) - (x1 * s);
+        row[i + h2] = (x1 * c) + (x0 * s);
+    } else {
+        row[i] = (x0 * c) + (x1 * s);
+        row[i + h2] = (x1 * c) - (x0 * s);
+    }
+}
+
+// Causal softmax in place, one wavefront per row i over j <= i:
+// m = MAX64, e = exp(S - m), Z = SUM64(e), P = e * (1 / Z).
+__global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t T) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= nbh * T) return;
+    const int64_t i = row % T;
+    float* p = P + row * T;
+    const int64_t n = i + 1;
+    float m = -__builtin_inff();
+    for (int64_t j = lane; j < n; j += 64) m = max_keep(m, p[j]);
+    m = wave_tree_max(m);
+    float acc = 0.0f;
+    for (int64_t j = lane; j < n; j += 64) {
+        const float e = exp_p(p[j] - m);
+        p[j] = e;
+        acc = acc + e;
+    }
+    const float Z = wave_tree_sum(acc);
+    const float rz = 1.0f / Z;
+    for (int64_t j = lane; j < n; j += 64) p[j] = p[j] * rz;
+}
+
+// D_i = DOT64 over the head dimension of dO and O, one wavefront per row.
+__global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, const float* __restrict__ O,
+                                                int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
+                                                float* __restrict__ D) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= B * H * T) return;
+    const int64_t i = row % T, z = row / T, b = z / H, h = z % H;
+    const int64_t off = (b * T + i) * ld + h * hd;
+    float acc = 0.0f;
+    for (int64_t c = lane; c < hd; c += 64) acc = __builtin_fmaf(dO[off + c], O[off + c], acc);
+    const float t = wave_tree_sum(acc);
+    if (lane == 0) D[row] = t;
+}
+
+// dS = (P * (dP - D_i)) * scale over j <= i, written over dP.
+__global__ __launch_bounds__(256) void k_softmax_bwd(const float* __restrict__ P, float* dP,
+                                                     const float* __restrict__ D, int64_t T, float scale) {
+    const int64_t i = blockIdx.x, z = blockIdx.y;
+    const int64_t base = (z * T + i) * T;
+    const float Di = D[z * T + i];
+    for (int64_t j = threadIdx.x; j <= i; j += blockDim.x)
+        dP[base + j] = (P[base + j] * (dP[base + j] - Di)) * scale;
+}
+
+// SwiGLU: sig = 1 / (1 + exp(-g)); a = (g * sig) * u.
+__global__ __launch_bounds__(256) void k_swiglu_fwd(const float* __restrict__ gu, int64_t rows, int64_t F,
+                                                    float* __restrict__ a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * F) return;
+    const int64_t n = idx / F, f = idx % F;
+    const float g = gu[n * 2 * F + f], u = gu[n * 2 * F + F + f];
+    const float sg = sigmoid_p(g);
+    a[idx] = (g * sg) * u;
+}
+
+// du = dA * (g * sig); dsilu = sig * (1 + g * (1 - sig)); dg = (dA * u) * dsilu.
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const float* __restrict__ dA, const float* __restrict__ gu,
+                                                    int64_t rows, int64_t F, float* __restrict__ dgu) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * F) return;
+    const int64_t n = idx / F, f = idx % F;
+    const float g = gu[n * 2 * F + f], u = gu[n * 2 * F + F + f];
+    const float da = dA[idx];
+    const float sg = sigmoid_p(g);
+    const float silu = g * sg;
+    const float dsilu = sg * (1.0f + (g * (1.0f - sg)));
+    dgu[n * 2 * F + F + f] = da * silu;
+    dgu[n * 2 * F + f] = (da * u) * dsilu;
+}
+
+// Cross-entropy, one wavefront per row: m = MAX64(l), Z = SUM64(exp(l - m)),
+// loss = log(Z) - (l_y - m); dl = ((exp(l - m) * (1/Z)) - [v == y]) * invN.
+// A target outside [0, V) raises *err and is read as 0 (no out-of-range read).
+__global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* __restrict__ tg, int64_t N,
+                                              int64_t V, float invN, float* __restrict__ loss_rows, float* dl,
+                                              int* err) {
+    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (n >= N) return;
+    const float* l = l_in + n * V;
+    int64_t y = tg[n];
+    if (y < 0 || y >= V) {
+        if (lane == 0) atomicOr(err, 2);
+        y = 0;
+    }
+    float m = -__builtin_inff();
+    for (int64_t v = lane; v < V; v += 64) m = max_keep(m, l[v]);
+    m = wave_tree_max(m);
+    float acc = 0.0f;
+    for (int64_t v = lane; v < V; v += 64) acc = acc + exp_p(l[v] - m);
+    const float Z = wave_tree_sum(acc);
+    const float ly = l[y];
+    if (lane == 0) loss_rows[n] = log_p(Z) - (ly - m);
+    const float rz = 1.0f / Z;
+    float* o = dl + n * V;
+    for (int64_t v = lane; v < V; v += 64) {
+        const float p = exp_p(l[v] - m) * rz;
+        const float t = (v == y) ? (p - 1.0f) : p;
+        o[v] = t * invN;
+    }
+}
+
+// out[0] = SUM64(v) * mul, one wavefront.
+__global__ __launch_bounds__(64) void k_sum64(const float* __restrict__ v, int64_t n, float mul, float* out) {
+    const int lane = threadIdx.x;
+    float acc = 0.0f;
+    for (int64_t i = lane; i < n; i += 64) acc = acc + v[i];
+    const float t = wave_tree_sum(acc);
+    if (lane == 0) out[0] = t * mul;
+}
+
+// Sort keys (id << 32 | n) in one workgroup (bitonic network in LDS). The keys
+// are distinct, so the sorted order is unique: ids ascending, positions
+// ascending within an id.
+constexpr int SORT_MAX = 8192;   // 64 KiB of LDS keys
+__global__ __launch_bounds__(1024) void k_sort_keys(const int32_t* __restrict__ ids, int64_t N, int64_t V,
+                                                    int64_t P, uint64_t* __restrict__ out) {
+    __shared__ uint64_t key[SORT_MAX];
+    for (int64_t q = threadIdx.x; q < P; q += blockDim.x) {
+        uint64_t k = ~0ull;
+        if (q < N) {
+            const int32_t id = ids[q];
+            if (id >= 0 && id < V) k = ((uint64_t)(uint32_t)id << 32) | (uint64_t)q;
+        }
+        key[q] = k;
+    }
+    __syncthreads();
+    for (int64_t size = 2; size <= P; size <<= 1) {
+        for (int64_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int64_t q = threadIdx.x; q < P; q += blockDim.x) {
+                const int64_t partner = q ^ stride;
+                if (partner > q) {
+                    const bool up = (q & size) == 0;
+                    const uint64_t a = key[q], b = key[partner];
+                    if ((a > b) == up) { key[q] = b; key[partner] = a; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int64_t q = threadIdx.x; q < P; q += blockDim.x) out[q] = key[q];
+}
+
+// For each segment head q (first sorted key of an id): acc = init(v); for the
+// segment's positions n in ascending order acc = acc + dh[n][c]; then write.
+__global__ __launch_bounds__(256) void k_scatter_segments(const uint64_t* __restrict__ key, int64_t N,
+                                                          const float* __restrict__ dh, int64_t d,
+                                                          const float* src_init, float* dst, int mode) {
+    const int64_t q = blockIdx.x;
+    const int64_t c = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+    const uint64_t kq = key[q];
+    if (kq == ~0ull || c >= d) return;
+    const uint32_t v = (uint32_t)(kq >> 32);
+    if (q > 0 && (uint32_t)(key[q - 1] >> 32) == v) return;    // not the head of its segment
+    float acc = src_init ? src_init[(int64_t)v * d + c] : 0.0f;
+    for (int64_t e = q; e < N; ++e) {
+        const uint64_t ke = key[e];
+        if ((uint32_t)(ke >> 32) != v || ke == ~0ull) break;
+        const int64_t n = (int64_t)(uint32_t)ke;
+        acc = acc + dh[n * d + c];
+    }
+    float* o = dst + (int64_t)v * d + c;
+    *o = mode ? *o + acc : acc;
+}
+
+__global__ __launch_bounds__(256) void k_add(float* out, const float* __restrict__ x, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = out[i] + x[i];
+}
+
+// AdamW, coupled form, one element per thread; the gradient accumulator is
+// reset to +0 after use.
+// m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*(g*g); mh = m/bc1; vh = v/bc2;
+// u = mh / (sqrt(vh) + eps); p = p - lr*(u + wd*p).
+__global__ __launch_bounds__(256) void k_adamw(float* __restrict__ p, float* __restrict__ g, float* __restrict__ m,
+                                               float* __restrict__ v, int64_t n, float lr, float b1, float b2,
+                                               float eps, float wd, float bc1, float bc2) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float omb1 = 1.0f - b1, omb2 = 1.0f - b2;
+    const float gi = g[i];
+    const float mi = (b1 * m[i]) + (omb1 * gi);
+    const float vi = (b2 * v[i]) + (omb2 * (gi * gi));
+    const float mh = mi / bc1;
+    const float vh = vi / bc2;
+    const float u = mh / (__builtin_sqrtf(vh) + eps);
+    const float pi = p[i];
+    p[i] = pi - (lr * (u + (wd * pi)));
+    m[i] = mi;
+    v[i] = vi;
+    g[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void k_unary(const float* __restrict__ x, float* __restrict__ y, int64_t n,
+                                               int which) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float v = x[i];
+    y[i] = which == 0 ? exp_p(v) : (which == 1 ? log_p(v) : sigmoid_p(v));
+}
+
+__global__ __launch_bounds__(256) void k_zero(float* x, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) x[i] = 0.0f;
+}
+
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// One FP32 MFMA per wavefront on lane-held operands; D holds R values per lane.
+template <int V>
+__global__ __launch_bounds__(64) void k_mfma_probe(const float* A, const float* B, const float* Cin, float* D) {
+    const int64_t t = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (V == 0) {
+        v32f c;
+        for (int r = 0; r < 32; ++r) c[r] = Cin[t * 32 + r];
+        c = __builtin_amdgcn_mfma_f32_32x32x1f32(A[t], B[t], c, 0, 0, 0);
+        for (int r = 0; r < 32; ++r) D[t * 32 + r] = c[r];
+    } else if (V == 1) {
+        v16f c;
+        for (int r = 0; r < 16; ++r) c[r] = Cin[t * 16 + r];
+        c = __builtin_amdgcn_mfma_f32_16x16x1f32(A[t], B[t], c, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) D[t * 16 + r] = c[r];
+    } else if (V == 2) {
+        v4f c;
+        for (int r = 0; r < 4; ++r) c[r] = Cin[t * 4 + r];
+        c = __builtin_amdgcn_mfma_f32_4x4x1f32(A[t], B[t], c, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) D[t * 4 + r] = c[r];
+    } else if (V == 3) {
+        v16f c;
+        for (int r = 0; r < 16; ++r) c[r] = Cin[t * 16 + r];
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(A[t], B[t], c, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) D[t * 16 + r] = c[r];
+    } else {
+        v4f c;
+        for (int r = 0; r < 4; ++r) c[r] = Cin[t * 4 + r];
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(A[t], B[t], c, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) D[t * 4 + r] = c[r];
+    }
+}
+
+inline int ok() { return hipGetLastError() == hipSuccess ? 0 : -3; }
+
+}  // namespace
+
+int gather_rows(const int32_t* ids, const float* table, int64_t V, int64_t d, int64_t N, float* out, int* err,
+                hipStream_t s) {
+    if (N < 0 || d <= 0 || V <= 0) return -1;
+    if (N == 0) return 0;
+    k_gather<<<blocks(N * d, 256), 256, 0, s>>>(ids, table, V, d, N, out, err);
+    return ok();
+}
+
+int rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float eps, float* y, float* r,
+                hipStream_t s) {
+    if (rows < 0 || d <= 0) return -1;
+    if (rows == 0) return 0;
+    k_rmsnorm_fwd<<<blocks(rows, 4), 256, 0, s>>>(x, w, rows, d, eps, y, r);
+    return ok();
+}
+
+int rmsnorm_bwd_dx(const float* dy, const float* x, const float* w, const float* r, int64_t rows, int64_t d,
+                   float* out, int accumulate, hipStream_t s) {
+    if (rows < 0 || d <= 0) return -1;
+    if (rows == 0) return 0;
+    k_rmsnorm_bwd_dx<<<blocks(rows, 4), 256, 0, s>>>(dy, x, w, r, rows, d, out, accumulate);
+    return ok();
+}
+
+int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows, int64_t d, float* part,
+                   float* dw, int mode, hipStream_t s) {
+    if (rows < 0 || d <= 0) return -1;
+    if (rows == 0) {
+        if (mode == 0) k_zero<<<blocks(d, 256), 256, 0, s>>>(dw, d);
+        return ok();
+    }
+    const int64_t nch = (rows + KC - 1) / KC;
+    k_rmsnorm_dw_part<<<dim3(blocks(d, 256), (unsigned)nch), 256, 0, s>>>(dy, x, r, rows, d, part);
+    k_fold_cols<<<blocks(d, 256), 256, 0, s>>>(part, nch, d, dw, mode);
+    return ok();
+}
+
+int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, const float* cosv,
+         const float* sinv, int backward, hipStream_t s) {
+    if (hd % 2 != 0 || B < 0 || T < 0 || H < 0) return -1;
+    const int64_t n = B * T * H * (hd / 2);
+    if (n == 0) return 0;
+    k_rope<<<blocks(n, 256), 256, 0, s>>>(x, B, T, H, hd, ld, cosv, sinv, backward);
+    return ok();
+}
+
+int softmax_causal(float* P, int64_t nbh, int64_t T, hipStream_t s) {
+    if (nbh < 0 || T < 0) return -1;
+    if (nbh * T == 0) return 0;
+    k_softmax<<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
+    return ok();
+}
+
+int attn_rowdot(const float* dO, const float* O, int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
+                float* D, hipStream_t s) {
+    if (B * H * T == 0) return 0;
+    k_rowdot<<<blocks(B * H * T, 4), 256, 0, s>>>(dO, O, B, H, T, hd, ld, D);
+    return ok();
+}
+
+int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t T, float scale, hipStream_t s) {
+    if (nbh * T == 0) return 0;
+    k_softmax_bwd<<<dim3((unsigned)T, (unsigned)nbh), 256, 0, s>>>(P, dP, D, T, scale);
+    return ok();
+}
+
+int swiglu_fwd(const float* gu, int64_t rows, int64_t F, float* a, hipStream_t s) {
+    if (rows * F == 0) return 0;
+    k_swiglu_fwd<<<blocks(rows * F, 256), 256, 0, s>>>(gu, rows, F, a);
+    return ok();
+}
+
+int swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float* dgu, hipStream_t s) {
+    if (rows * F == 0) return 0;
+    k_swiglu_bwd<<<blocks(rows * F, 256), 256, 0, s>>>(dA, gu, rows, F, dgu);
+    return ok();
+}
+
+int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, float* loss_rows, float* dl,
+                  int* err, hipStream_t s) {
+    if (N < 0 || V <= 0) return -1;
+    if (N == 0) return 0;
+    const float invN = 1.0f / (float)N;
+    k_xent<<<blocks(N, 4), 256, 0, s>>>(logits, tg, N, V, invN, loss_rows, dl, err);
+    return ok();
+}
+
+int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s) {
+    k_sum64<<<1, 64, 0, s>>>(v, n, mul, out);
+    return ok();
+}
+
+int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, const float* src_init,
+                  float* dst, int mode, uint64_t* keys, hipStream_t s) {
+    if (N < 0 || d <= 0 || V <= 0 || N > SORT_MAX) return -2;
+    if (N == 0) return 0;
+    int64_t P = 1;
+    while (P < N) P <<= 1;
+    k_sort_keys<<<1, 1024, 0, s>>>(ids, N, V, P, keys);
+    k_scatter_segments<<<dim3((unsigned)N, blocks(d, 256)), 256, 0, s>>>(keys, N, dh, d, src_init, dst, mode);
+    return ok();
+}
+
+int add_inplace(float* out, const float* x, int64_t n, hipStream_t s) {
+    if (n <= 0) return n == 0 ? 0 : -1;
+    k_add<<<blocks(n, 256), 256, 0, s>>>(out, x, n);
+    return ok();
+}
+
+int adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float b1, float b2, float eps, float wd,
+          float bc1, float bc2, hipStream_t s) {
+    if (n <= 0) return n == 0 ? 0 : -1;
+    k_adamw<<<blocks(n, 256), 256, 0, s>>>(p, g, m, v, n, lr, b1, b2, eps, wd, bc1, bc2);
+    return ok();
+}
+
+int exp_array(const float* x, float* y, int64_t n, int which, hipStream_t s) {
+    if (n <= 0 || which < 0 || which > 2) return n == 0 ? 0 : -1;
+    k_unary<<<blocks(n, 256), 256, 0, s>>>(x, y, n, which);
+    return ok();
+}
+
+int fill_zero(float* x, int64_t n, hipStream_t s) {
+    if (n <= 0) return n == 0 ? 0 : -1;
+    k_zero<<<blocks(n, 256), 256, 0, s>>>(x, n);
+    return ok();
+}
+
+int mfma_probe(int variant, const float* A, const float* B, const float* C, float* D, int64_t nwaves,
+               hipStream_t s) {
+    if (nwaves <= 0) return -1;
+    const dim3 g((unsigned)nwaves);
+    switch (variant) {
+        case 0: k_mfma_probe<0><<<g, 64, 0, s>>>(A, B, C, D); break;
+        case 1: k_mfma_probe<1><<<g, 64, 0, s>>>(A, B, C, D); break;
+        case 2: k_mfma_probe<2><<<g, 64, 0, s>>>(A, B, C, D); break;
+        case 3: k_mfma_probe<3><<<g, 64, 0, s>>>(A, B, C, D); break;
+        case 4: k_mfma_probe<4><<<g, 64, 0, s>>>(A, B, C, D); break;
+        default: return -1;
+    }
+    return ok();
+}
+
+}  // namespace mlb

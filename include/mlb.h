@@ -1,0 +1,142 @@
+/*
+ * mlb.h - C ABI of the bitwise-reproducible FP32 training step (MI355X, gfx950).
+ *
+ * One training step of a Llama-style decoder - embedding lookup, pre-norm
+ * RMSNorm, rotary causal attention, SwiGLU, untied (or tied) output table,
+ * cross-entropy, backward, fixed-order accumulation of micro-batch gradients
+ * and AdamW - computed under the frozen numerical profile MLB-P1, so that every
+ * output bit depends only on the inputs. The model and optimiser follow the
+ * MojoLearn 162M model card ("Compared with GPT-3 Small" and "Training"
+ * tables); the bit-identity contract follows the mojolearn PyPI page ("What
+ * bitwise identity means": reduction order, partitioning, FMA policy, flush
+ * seams, transcendental spellings and tie rules are fixed, and a request that
+ * cannot be met is refused by name instead of falling back).
+ *
+ * Memory: the caller owns one device arena (mlb_workspace_bytes) and the HIP
+ * stream; the library owns the handle and a 64-byte pinned host staging buffer.
+ * Every call enqueues on the caller's stream. mlb_forward_loss, mlb_save,
+ * mlb_load and mlb_read synchronise that stream; the others do not.
+ * A handle is not thread-safe. Errors are returned as negative mlb_status
+ * values; mlb_last_error_message() (thread-local) gives the detail.
+ * NaN and Inf are not checked: they are deterministic bit patterns too, but
+ * NaN payload bits are not part of the contract.
+ */
+#ifndef MLB_H
+#define MLB_H
+#include <stddef.h>
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLB_ABI_VERSION 1u
+#define MLB_PROFILE_VERSION 1u /* MLB-P1 */
+
+typedef int32_t mlb_status;
+#define MLB_OK 0
+#define MLB_E_INVALID_ARG (-1)      /* null pointer, bad size, bad enum */
+#define MLB_E_UNSUPPORTED (-2)      /* named refusal: device or config outside the profile */
+#define MLB_E_DEVICE (-3)           /* a HIP runtime call or kernel launch failed */
+#define MLB_E_ARENA_TOO_SMALL (-4)
+#define MLB_E_BAD_TOKEN (-5)        /* an input or target id outside [0, vocab) */
+#define MLB_E_STATE (-6)            /* call order violated */
+#define MLB_E_CORRUPT (-7)          /* checkpoint bytes fail a digest or size check */
+#define MLB_E_PROFILE_MISMATCH (-8) /* checkpoint written under another format or profile */
+#define MLB_E_CONFIG_MISMATCH (-9)  /* checkpoint written for another model config */
+#define MLB_E_IO (-10)              /* host buffer too small */
+
+/* Model shape and optimiser constants. abi_version must be MLB_ABI_VERSION.
+ * d_model = n_heads * head_dim; head_dim even; d_model and ffn_hidden multiples
+ * of 32; batch * seq_len <= 8192 tokens per micro-batch. */
+typedef struct mlb_config {
+    uint32_t abi_version;
+    uint32_t vocab, d_model, n_layers, n_heads, head_dim, ffn_hidden, tied, batch, seq_len;
+    float rope_theta, rms_eps, beta1, beta2, adam_eps, weight_decay;
+} mlb_config;
+
+typedef struct mlb_model mlb_model;
+
+typedef enum mlb_which { MLB_PARAMS = 0, MLB_GRAD = 1, MLB_ADAM_M = 2, MLB_ADAM_V = 3 } mlb_which;
+
+/* Parameter count in canonical order: E_in [V,d]; per layer attn_norm [d],
+ * Wq, Wk, Wv, Wo [d,d], mlp_norm [d], Wg, Wu [F,d], Wd [d,F]; W_out [V,d] when
+ * untied. Linear weights are [out_features, in_features] (model card, "Anywhere
+ * else: safetensors + PyTorch"). Returns -1 for an invalid config. */
+int64_t mlb_param_count(const mlb_config* cfg);
+
+/* Device bytes the arena must hold for cfg (params, gradient accumulator,
+ * both moments, stored activations and scratch of one micro-batch). */
+mlb_status mlb_workspace_bytes(const mlb_config* cfg, size_t* bytes);
+
+/* Creates a model on the current HIP device. init_params_host: host float32
+ * array of mlb_param_count(cfg) values (step-0 parameters), read during the
+ * call. dev_arena: caller-owned device memory of arena_bytes, 256-byte aligned,
+ * untouched by anything else while the model lives. hip_stream: a hipStream_t
+ * (may be null). Moments and the gradient accumulator start at +0, step 0.
+ * Refuses a device that is not gfx950 (MLB_E_UNSUPPORTED). */
+mlb_status mlb_init(const mlb_config* cfg, const float* init_params_host, void* dev_arena, size_t arena_bytes,
+                    void* hip_stream, mlb_model** out);
+
+/* Forward pass and loss of one micro-batch: d_inputs and d_targets are device
+ * int32 arrays of batch*seq_len ids (row-major [batch, seq_len]), read before
+ * the call returns. Writes the shard loss (mean over the micro-batch) to
+ * *out_loss_host and keeps the activations for mlb_backward. Synchronises the
+ * stream. An id outside [0, vocab) gives MLB_E_BAD_TOKEN and no usable forward. */
+mlb_status mlb_forward_loss(mlb_model* m, const int32_t* d_inputs, const int32_t* d_targets, float* out_loss_host);
+
+/* Backward of the last forward; folds its gradient g into the accumulator,
+ * G = G + g (call order = micro-batch order). MLB_E_STATE without a forward. */
+mlb_status mlb_backward(mlb_model* m);
+
+/* One AdamW step with learning rate lr on the accumulated G, then G = +0.
+ * MLB_E_STATE when no backward ran since the last step. */
+mlb_status mlb_adamw_step(mlb_model* m, float lr);
+
+/* Exact state bytes (MLBC v1): 256-byte header (magic "MLBCKPT1", format,
+ * profile, config, step, parameter count, SHA-256 of params, m, v and of the
+ * header itself) followed by params, m and v as little-endian float32. The
+ * bytes are a pure function of the state. host_buf NULL: *len = size only.
+ * MLB_E_STATE while gradients are pending; MLB_E_IO if cap is too small. */
+mlb_status mlb_save(const mlb_model* m, void* host_buf, size_t cap, size_t* len);
+
+/* Restores params, moments and step from mlb_save bytes. Verifies magic,
+ * format and profile (MLB_E_PROFILE_MISMATCH), config (MLB_E_CONFIG_MISMATCH),
+ * size and every digest (MLB_E_CORRUPT) before touching the state. */
+mlb_status mlb_load(mlb_model* m, const void* host_buf, size_t len);
+
+/* Copies a state array (mlb_param_count floats) to host memory. */
+mlb_status mlb_read(const mlb_model* m, mlb_which which, void* host_dst, size_t bytes);
+
+/* Copies an activation of the last forward to host memory (stage ids: 0 layer
+ * input, 1 attention-norm output, 2 its 1/rms, 3 q|k|v after rotation, 4 P,
+ * 5 attention output, 6 mid-layer residual, 7 MLP-norm output, 8 its 1/rms,
+ * 9 g|u, 10 SwiGLU output, 11 final hidden, 12 d-logits, 13 per-row losses).
+ * *count receives the element count; host_dst may be NULL to query it. */
+mlb_status mlb_read_stage(const mlb_model* m, int stage, int layer, void* host_dst, size_t bytes, size_t* count);
+
+/* Launch statistics (this library's own tracing). When enabled, every kernel
+ * launch of the step is bracketed by HIP events on the model's stream and
+ * aggregated per call site: launch count, total milliseconds, algorithmic
+ * FLOPs (2 per valid multiply-add of a contraction) and algorithmic HBM bytes
+ * (minimal reads + writes of a row or elementwise kernel). Enabling clears
+ * the aggregates. mlb_stats_read synchronises the stream and copies up to cap
+ * entries; *n receives the number of sites. */
+typedef struct mlb_stat {
+    char site[48];
+    char kernel[96];
+    int64_t launches;
+    double ms, flops, bytes;
+} mlb_stat;
+mlb_status mlb_stats_enable(mlb_model* m, int on);
+mlb_status mlb_stats_read(mlb_model* m, mlb_stat* out, int cap, int* n);
+
+uint64_t mlb_step(const mlb_model* m);
+mlb_status mlb_destroy(mlb_model* m);
+const char* mlb_status_name(mlb_status s);
+const char* mlb_last_error_message(void);
+uint32_t mlb_profile_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

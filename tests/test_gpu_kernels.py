@@ -1,0 +1,334 @@
+"""Kernel-level parity on the GPU against the oracle, called through the C ABI:
+the matrix-core probe, exp/log spellings, the G1024 contraction on odd shapes,
+layouts, causal ranges and segments, launch-geometry perturbation, and each row
+operation of the step (RMSNorm, RoPE, attention, SwiGLU, cross-entropy,
+embedding scatter, AdamW)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_bits, dev, empty, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mlb():
+    import bitwise_reproducible_fp32_amd as m
+    return m
+
+
+# ------------------------------------------------------------ matrix-core probe
+PROBE = {0: (32, 1), 1: (16, 1), 2: (4, 1), 3: (16, 2), 4: (4, 4)}   # variant: (outputs per lane, K)
+
+
+def rnd_operands(rng, n):
+    cls = rng.integers(0, 4, n)
+    mant = rng.uniform(1, 2, n) * np.where(rng.integers(0, 2, n) == 0, 1, -1)
+    e = np.where(cls == 0, rng.integers(-20, 21, n), np.where(cls == 2, rng.integers(-80, -59, n),
+                                                             rng.integers(-130, 121, n)))
+    x = (mant * np.exp2(e.astype(np.float64))).astype(np.float32)
+    spec = rng.integers(0, 8, n)
+    x = np.where((cls == 3) & (spec == 0), np.float32(0.0), x)
+    x = np.where((cls == 3) & (spec == 1), np.float32(-0.0), x)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("variant", sorted(PROBE))
+def test_mfma_is_an_ascending_fma_chain(mlb, variant):
+    """Every FP32 MFMA output equals fma chains over its k-lanes in ascending
+    order, with IEEE denormals (the fact the contraction kernels rely on)."""
+    R, K = PROBE[variant]
+    nw = 128 + 512
+    rng = np.random.default_rng(variant)
+    A = np.zeros(nw * 64, np.float32)
+    B = np.zeros(nw * 64, np.float32)
+    # waves 0..63: one-hot A lanes, waves 64..127: one-hot B lanes (layout discovery)
+    for w in range(64):
+        A[w * 64 + w] = 1.0; B[w * 64:(w + 1) * 64] = 1.0
+        A[(64 + w) * 64:(65 + w) * 64] = 1.0; B[(64 + w) * 64 + w] = 1.0
+    A[128 * 64:] = rnd_operands(rng, (nw - 128) * 64)
+    B[128 * 64:] = rnd_operands(rng, (nw - 128) * 64)
+    Cin = np.zeros(nw * 64 * R, np.float32)
+    Cin[128 * 64 * R:] = rnd_operands(rng, (nw - 128) * 64 * R)
+    D = empty(nw * 64 * R)
+    mlb.diag_mfma(variant, dev(A), dev(B), dev(Cin), D, nw)
+    out = host(D).reshape(nw, 64, R)
+    SA = [[np.nonzero(out[:64, l, r])[0] for r in range(R)] for l in range(64)]
+    SB = [[np.nonzero(out[64:128, l, r])[0] for r in range(R)] for l in range(64)]
+    assert all(len(SA[l][r]) == K and len(SB[l][r]) == K for l in range(64) for r in range(R))
+    got = out[128:]
+    a = A.reshape(nw, 64)[128:]
+    b = B.reshape(nw, 64)[128:]
+    c = Cin.reshape(nw, 64, R)[128:]
+    for l in range(64):
+        for r in range(R):
+            acc = c[:, l, r]
+            for k in range(K):      # ascending lane order = ascending k
+                acc = oracle.fma(a[:, SA[l][r][k]], b[:, SB[l][r][k]], acc)
+            assert_bits(f"variant {variant} lane {l} reg {r}", got[:, l, r], acc)
+
+
+# ------------------------------------------------------------------ exp / log
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_elementary_spellings_match_oracle(mlb, which):
+    u = np.arange(0, 1 << 32, 257, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    y = empty(x.size)
+    mlb.unary(dev(x), y, x.size, which)
+    if which == 2:
+        want = np.empty_like(x)
+        oracle.lib().orc_sigmoid_array(x, want, x.size)
+    else:
+        want = (oracle.exp, oracle.log)[which](x)
+    assert_bits(["exp", "log", "sigmoid"][which], host(y), want)
+
+
+# --------------------------------------------------------------- contractions
+def make(rng, shape):
+    return rng.uniform(-1, 1, shape).astype(np.float32)
+
+
+def orc_contract(A, B, M, N, K, lda, a_kc, ldb, b_kc, kseg=0, krange=0, outmask=0, mode=0, scale=1.0, C0=None):
+    sam, sak = (lda, 1) if a_kc else (1, lda)
+    sbk, sbn = (1, ldb) if b_kc else (ldb, 1)
+    C = np.zeros(M * N, np.float32) if C0 is None else C0.copy().ravel()
+    return oracle.gemm(A.ravel(), B.ravel(), M, N, K, sam, sak, sbk, sbn, C=C, kseg=kseg or K, mode=mode,
+                       scale=scale, krange=krange, outmask=outmask).reshape(M, N)
+
+
+SHAPES = [(1, 1, 1), (37, 767, 5), (129, 3, 257), (200, 2100, 130), (64, 64, 64), (300, 1030, 70)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn", "tt"])
+def test_contraction_odd_shapes(mlb, M, K, N, layout):
+    rng = np.random.default_rng(M + K + N)
+    a_kc, b_kc = layout[0] == "n", layout[1] == "t"
+    A = make(rng, (M, K) if a_kc else (K, M))
+    B = make(rng, (N, K) if b_kc else (K, N))
+    lda = K if a_kc else M
+    ldb = K if b_kc else N
+    want = orc_contract(A, B, M, N, K, lda, a_kc, ldb, b_kc)
+    for tile in (0, 1):
+        C = empty(M * N)
+        mlb.gemm(dev(A), dev(B), C, M, N, K, lda, a_kc, ldb, b_kc, N, tile=tile)
+        assert_bits(f"{layout} tile {tile}", host(C).reshape(M, N), want)
+    C = empty(M * N)
+    mlb.gemm(dev(A), dev(B), C, M, N, K, lda, a_kc, ldb, b_kc, N, simple=1)
+    assert_bits(f"{layout} simple", host(C).reshape(M, N), want)
+
+
+@pytest.mark.parametrize("K", [2048, 3000, 8192])
+def test_split_chunks_same_bits(mlb, K):
+    """Per-chunk partials folded by a second kernel equal the in-kernel fold."""
+    rng = np.random.default_rng(K)
+    M, N = 96, 160
+    A, B = make(rng, (K, M)), make(rng, (K, N))
+    want = orc_contract(A, B, M, N, K, M, False, N, False)
+    ws = empty((K + 1023) // 1024 * M * N)
+    for split in (0, 1):
+        C = empty(M * N)
+        mlb.gemm(dev(A), dev(B), C, M, N, K, M, False, N, False, N, split=split, ws=ws)
+        assert_bits(f"split {split}", host(C).reshape(M, N), want)
+
+
+def test_segments_and_modes(mlb):
+    rng = np.random.default_rng(5)
+    M, d, F = 70, 96, 1056   # two segments of 1056 -> chunks 1024 + 32 each
+    A, B = make(rng, (M, 2 * F)), make(rng, (2 * F, d))
+    C0 = make(rng, (M, d))
+    want = orc_contract(A, B, M, d, 2 * F, 2 * F, True, d, False, kseg=F, mode=1, C0=C0)
+    C = dev(C0.copy())
+    mlb.gemm(dev(A), dev(B), C, M, d, 2 * F, 2 * F, True, d, False, d, kseg=F, mode=1)
+    assert_bits("segments accumulate", host(C), want)
+    want = orc_contract(A, B, M, d, 2 * F, 2 * F, True, d, False, kseg=F, mode=2, scale=0.375)
+    C = empty(M * d)
+    mlb.gemm(dev(A), dev(B), C, M, d, 2 * F, 2 * F, True, d, False, d, kseg=F, mode=2, scale=0.375)
+    assert_bits("segments scaled", host(C).reshape(M, d), want)
+
+
+@pytest.mark.parametrize("krange", [1, 2])
+@pytest.mark.parametrize("T,hd", [(64, 8), (300, 5), (1100, 64)])
+def test_causal_ranges(mlb, krange, T, hd):
+    rng = np.random.default_rng(T * krange)
+    P = make(rng, (T, T))
+    V = make(rng, (T, hd))
+    if krange == 1:   # O[i] = sum_{j<=i} P[i,j] V[j]
+        want = orc_contract(P, V, T, hd, T, T, True, hd, False, krange=1)
+        a_kc = True
+    else:             # dV[j] = sum_{i>=j} P[i,j] dO[i]
+        want = orc_contract(P, V, T, hd, T, T, False, hd, False, krange=2)
+        a_kc = False
+    for simple in (0, 1):
+        C = empty(T * hd)
+        mlb.gemm(dev(P), dev(V), C, T, hd, T, T, a_kc, hd, False, hd, krange=krange, simple=simple)
+        assert_bits(f"krange {krange} simple {simple}", host(C).reshape(T, hd), want)
+
+
+def test_outmask_scores(mlb):
+    rng = np.random.default_rng(9)
+    T, hd = 300, 64
+    q, k = make(rng, (T, hd)), make(rng, (T, hd))
+    sc = np.float32(0.125)
+    want = orc_contract(q, k, T, T, hd, hd, True, hd, True, mode=2, scale=sc, outmask=1)
+    C = dev(np.full((T, T), 7.0, np.float32))
+    mlb.gemm(dev(q), dev(k), C, T, T, hd, hd, True, hd, True, T, mode=2, scale=sc, outmask=1)
+    got = host(C)
+    low = np.tril(np.ones((T, T), bool))
+    assert_bits("lower triangle", got[low], want[low])
+    assert np.all(got[~low] == 7.0)
+
+
+SWEEP = [(8192, 768, 2304), (8192, 768, 2048), (8192, 2048, 768), (8192, 768, 50257)]
+
+
+@pytest.mark.parametrize("M,K,N", SWEEP)
+def test_sweep_forward_shapes_sampled_rows(mlb, M, K, N):
+    rng = np.random.default_rng(7)
+    X, W = make(rng, (M, K)), make(rng, (N, K))
+    C = empty(M * N)
+    mlb.gemm(dev(X), dev(W), C, M, N, K, K, True, K, True, N)
+    got = host(C).reshape(M, N)
+    rows = np.array([0, 1, 63, 64, 127, 128, 4095, 4096, M - 2, M - 1])
+    want = oracle.gemm_rows(X.ravel(), W.ravel(), M, N, K, K, 1, 1, K, rows)
+    assert_bits(f"{M}x{K}x{N}", got[rows], want)
+
+
+def test_sweep_weight_gradient_shape(mlb):
+    """768 x 8192 x 768: dY^T X over 8192 rows (8 chunks), both fold paths."""
+    rng = np.random.default_rng(8)
+    n, o, i = 8192, 768, 768
+    dY, X = make(rng, (n, o)), make(rng, (n, i))
+    rows = np.array([0, 5, 383, 767])
+    want = oracle.gemm_rows(dY.ravel(), X.ravel(), o, i, n, 1, o, i, 1, rows)
+    ws = empty(8 * o * i)
+    for split in (0, 1):
+        C = empty(o * i)
+        mlb.gemm(dev(dY), dev(X), C, o, i, n, o, False, i, False, i, split=split, ws=ws)
+        assert_bits(f"dW split {split}", host(C).reshape(o, i)[rows], want)
+
+
+# ------------------------------------------------------------- row operations
+@pytest.mark.parametrize("rows,d", [(8192, 767), (8192, 768), (3, 32)])
+def test_rmsnorm(mlb, rows, d):
+    rng = np.random.default_rng(d)
+    x, w, dy = make(rng, (rows, d)), make(rng, d), make(rng, (rows, d))
+    eps = np.float32(1e-6)
+    y, r = empty(rows * d), empty(rows)
+    xd_shape = dev(x)
+    mlb.rmsnorm_fwd(xd_shape, dev(w), eps, y, r)
+    yo, ro = oracle.rmsnorm_fwd(x, w, eps)
+    assert_bits("y", host(y).reshape(rows, d), yo)
+    assert_bits("r", host(r), ro)
+    dx, dw = empty(rows * d), empty(d)
+    ws = empty(((rows + 1023) // 1024) * d)
+    mlb.rmsnorm_bwd(dev(dy), xd_shape, dev(w), dev(ro), dx, dw, ws)
+    dxo, dwo = oracle.rmsnorm_bwd(dy, x, w, ro)
+    assert_bits("dx", host(dx).reshape(rows, d), dxo)
+    assert_bits("dw", host(dw), dwo)
+
+
+def test_rope(mlb):
+    rng = np.random.default_rng(2)
+    B, T, H, hd = 2, 2048, 3, 64
+    ld = 3 * H * hd
+    x = make(rng, (B * T, ld))
+    c, s = oracle.rope_table(T, hd, 10000.0)
+    for bwd in (0, 1):
+        want = x.copy()
+        fn = oracle.lib().orc_rope_bwd if bwd else oracle.lib().orc_rope_fwd
+        fn(oracle._p(want), B, T, H, hd, ld, c, s)
+        xd = dev(x)
+        mlb.rope(xd, B, T, H, hd, ld, 10000.0, backward=bwd)
+        assert_bits(f"rope bwd={bwd}", host(xd), want)
+
+
+@pytest.mark.parametrize("BH,T,hd", [(2, 64, 8), (3, 300, 5), (2, 1100, 64)])
+def test_attention_fwd_bwd(mlb, BH, T, hd):
+    rng = np.random.default_rng(T + hd)
+    q, k, v, dO = (make(rng, (BH, T, hd)) for _ in range(4))
+    P, O = empty(BH * T * T), empty(BH * T * hd)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    mlb.attention_fwd(BH, 1, T, hd, qd, kd, vd, hd, P, O, hd)
+    Po, Oo = oracle.attention_fwd(q, k, v)
+    low = np.tril(np.ones((T, T), bool))
+    Pg = host(P).reshape(BH, T, T)
+    assert_bits("P", Pg[:, low], Po[:, low])
+    assert_bits("O", host(O).reshape(BH, T, hd), Oo)
+    dq, dk, dv = empty(BH * T * hd), empty(BH * T * hd), empty(BH * T * hd)
+    ws = empty(BH * T * T + BH * T)
+    mlb.attention_bwd(BH, 1, T, hd, qd, kd, vd, hd, P, O, dev(dO), hd, dq, dk, dv, ws)
+    dqo, dko, dvo = oracle.attention_bwd(q, k, v, Po, Oo, dO)
+    assert_bits("dq", host(dq).reshape(BH, T, hd), dqo)
+    assert_bits("dk", host(dk).reshape(BH, T, hd), dko)
+    assert_bits("dv", host(dv).reshape(BH, T, hd), dvo)
+
+
+def test_swiglu(mlb):
+    rng = np.random.default_rng(3)
+    rows, F = 4096, 1024
+    gu = (make(rng, (rows, 2 * F)) * 8).astype(np.float32)
+    dA = make(rng, (rows, F))
+    a = empty(rows * F)
+    gud = dev(gu)
+    mlb.swiglu_fwd(gud, rows, F, a)
+    ao = np.empty((rows, F), np.float32)
+    oracle.lib().orc_swiglu_fwd(gu, rows, F, 2 * F, ao, F)
+    assert_bits("a", host(a).reshape(rows, F), ao)
+    dgu = empty(rows * 2 * F)
+    mlb.swiglu_bwd(dev(dA), gud, rows, F, dgu)
+    dguo = np.empty_like(gu)
+    oracle.lib().orc_swiglu_bwd(dA, F, gu, rows, F, 2 * F, dguo)
+    assert_bits("dgu", host(dgu).reshape(rows, 2 * F), dguo)
+
+
+@pytest.mark.parametrize("N,V", [(64, 256), (37, 50257)])
+def test_cross_entropy(mlb, N, V):
+    rng = np.random.default_rng(V)
+    logits = (make(rng, (N, V)) * 4).astype(np.float32)
+    tg = rng.integers(0, V, N).astype(np.int32)
+    rows, dl, loss = empty(N), empty(N * V), empty(1)
+    mlb.cross_entropy(dev(logits), dev(tg), N, V, rows, dl, loss)
+    lo, ro, dlo = oracle.cross_entropy(logits, tg)
+    assert_bits("rows", host(rows), ro)
+    assert_bits("dl", host(dl).reshape(N, V), dlo)
+    assert_bits("loss", host(loss), np.float32([lo]))
+
+
+def test_cross_entropy_bad_target_refused(mlb):
+    logits = np.zeros((4, 10), np.float32)
+    tg = np.array([0, 1, 10, 2], np.int32)
+    with pytest.raises(mlb.MlbError) as e:
+        mlb.cross_entropy(dev(logits), dev(tg), 4, 10, empty(4), empty(40), empty(1))
+    assert e.value.name == "MLB_E_BAD_TOKEN"
+
+
+def test_embed_scatter_zipf(mlb):
+    from bitwise_reproducible_fp32_amd import inputs as I
+    N, V, d = 8192, 50257, 768
+    ids = I.zipf_ids(N, V, 5)
+    dh = make(np.random.default_rng(4), (N, d))
+    base = make(np.random.default_rng(6), (V, d))
+    want = oracle.embed_scatter(ids, dh, base)
+    dE = dev(base)
+    mlb.embed_scatter(dev(ids), dev(dh), N, d, V, dE, empty(2 * 8192 * 2))
+    assert_bits("dE", host(dE), want)
+
+
+def test_adamw(mlb):
+    rng = np.random.default_rng(11)
+    n = 1 << 20
+    p, g = make(rng, n), (make(rng, n) * np.exp2(rng.integers(-20, 3, n))).astype(np.float32)
+    m, v = make(rng, n) * 0.01, np.abs(make(rng, n)) * 1e-4
+    m, v = m.astype(np.float32), v.astype(np.float32)
+    b1, b2, eps, wd, lr, t = np.float32(0.9), np.float32(0.95), np.float32(1e-8), np.float32(0.1), np.float32(6e-4), 7
+    pd, gd, md, vd = dev(p), dev(g), dev(m), dev(v)
+    mlb.adamw(pd, gd, md, vd, n, lr, b1, b2, eps, wd, t)
+    po, mo, vo = p.copy(), m.copy(), v.copy()
+    oracle.lib().orc_adamw(po, g, mo, vo, n, lr, b1, b2, eps, wd, oracle.lib().orc_bias_correction(b1, t),
+                           oracle.lib().orc_bias_correction(b2, t))
+    assert_bits("p", host(pd), po)
+    assert_bits("m", host(md), mo)
+    assert_bits("v", host(vd), vo)
+    assert np.all(host(gd) == 0) and not np.any(np.signbit(host(gd)))

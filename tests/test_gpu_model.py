@@ -1,0 +1,115 @@
+"""End-to-end parity of the training step on the GPU against the oracle:
+the byte LM's first 4 steps, the 64 + save + fresh process + load + 64 resume
+run against 128 uninterrupted steps, the 6-layer decoder's steps 1-3, and
+run-to-run identity. Expected digests come from tests/golden (written by the
+oracle); the first step is also compared stage by stage with a live oracle."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from bitwise_reproducible_fp32_amd import inputs as I
+from gpu_util import assert_bits, dev, first_divergence
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLD, f"{name}.json")) as f:
+        return json.load(f)
+
+
+def hx(x) -> str:
+    return np.float32(x).tobytes()[::-1].hex()
+
+
+def sha(a) -> str:
+    return oracle.sha256(np.ascontiguousarray(a).tobytes())
+
+
+def run_gpu(name, cfg, steps, model=None, start=1, data_name=None):
+    import bitwise_reproducible_fp32_amd as mlb
+    data_name = data_name or name
+    m = model or mlb.Model(cfg, I.init_params(cfg))
+    recs = []
+    for s in range(start, start + steps):
+        losses = []
+        for mb in range(cfg["micro"]):
+            x, y = I.batch_for(data_name, cfg, s, mb)
+            losses.append(m.forward_loss(dev(x.astype(np.int32)), dev(y.astype(np.int32))))
+            m.backward()
+        grad = sha(m.read(mlb.GRAD))
+        lr = I.lr_at(data_name, s)
+        m.adamw_step(lr)
+        recs.append(dict(step=s, lr=hx(lr), losses=[hx(l) for l in losses], grad=grad,
+                         params=sha(m.read(mlb.PARAMS)), adam_m=sha(m.read(mlb.ADAM_M)),
+                         adam_v=sha(m.read(mlb.ADAM_V)), ckpt=oracle.sha256(m.save())))
+    return m, recs
+
+
+def compare(recs, gold):
+    for r, g in zip(recs, gold):
+        for key in ("lr", "losses", "grad", "params", "adam_m", "adam_v", "ckpt"):
+            assert r[key] == g[key], f"step {r['step']} {key}: {r[key]} != {g[key]}"
+
+
+def test_c0_first_step_stages_match_live_oracle():
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c0")
+    p = I.init_params(cfg)
+    x, y = I.c0_batch(0)
+    g = mlb.Model(cfg, p)
+    o = oracle.Model(cfg, p)
+    lg = g.forward_loss(dev(x.astype(np.int32)), dev(y.astype(np.int32)))
+    lo = o.forward(x, y)
+    report = first_divergence(g, o, cfg)
+    assert report == "forward stages all equal", report
+    assert lg.tobytes() == lo.tobytes()
+    g.backward()
+    o.backward()
+    assert_bits("G after one backward", g.read(mlb.GRAD), o.grad)
+    g.adamw_step(1e-3)
+    o.adamw(np.float32(1e-3))
+    for w, name in ((mlb.PARAMS, "params"), (mlb.ADAM_M, "m"), (mlb.ADAM_V, "v")):
+        assert_bits(name, g.read(w), o.read(w))
+
+
+def test_c0_four_steps_bit_exact():
+    gold = golden("c0")
+    _, recs = run_gpu("c0", I.make_config("c0"), 4)
+    compare(recs, gold["steps"])
+
+
+def test_c0_run_to_run():
+    cfg = I.make_config("c0")
+    _, a = run_gpu("c0", cfg, 2)
+    _, b = run_gpu("c0", cfg, 2)
+    assert a == b
+
+
+def test_c2_resume_across_processes(tmp_path):
+    gold = golden("c2")
+    cfg = I.make_config("c0")
+    m, first = run_gpu("c2", cfg, 64, data_name="c0")
+    compare(first, gold["steps"][:64])
+    blob = m.save()
+    assert oracle.sha256(blob) == gold["ckpt_step64"]
+    ck = tmp_path / "step64.mlbc"
+    ck.write_bytes(blob)
+    out = tmp_path / "second.json"
+    worker = os.path.join(os.path.dirname(os.path.abspath(__file__)), "resume_worker.py")
+    r = subprocess.run([sys.executable, worker, str(ck), str(out)], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
+    second = json.loads(out.read_text())
+    compare(second, gold["steps"][64:])
+
+
+def test_c3_three_steps_bit_exact():
+    gold = golden("c3")
+    _, recs = run_gpu("c3", I.make_config("c3"), 3)
+    compare(recs, gold["steps"])
