@@ -134,6 +134,11 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     stats = model.stats()
     model.stats_enable(False)
+    for st in sorted(stats, key=lambda t: -t["ms"]):
+        rate = (f"{st['flops'] / st['ms'] / 1e9:7.2f} TFLOP/s" if st["flops"] else
+                f"{st['bytes'] / st['ms'] / 1e6:7.1f} GB/s")
+        print(f"# {st['ms'] / a.steps:9.2f} ms/step {st['launches'] // a.steps:5d}x {rate}  {st['site']:14s} "
+              f"{st['kernel']}", file=sys.stderr)
 
     tokens = S * B * T
     fpt = flops_per_token(cfg)

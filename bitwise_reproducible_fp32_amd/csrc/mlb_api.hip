@@ -132,6 +132,7 @@ constexpr int64_t MAX_TOKENS = 8192;
 
 struct Sizes {
     int64_t V, d, L, H, hd, F, B, T, N, P;
+    int64_t ldV;   // logits row stride: V rounded up to 4 so rows take float4 loads
     bool tied;
 };
 
@@ -164,6 +165,7 @@ Sizes sizes_of(const mlb_config* c) {
     Sizes s;
     s.V = c->vocab; s.d = c->d_model; s.L = c->n_layers; s.H = c->n_heads; s.hd = c->head_dim;
     s.F = c->ffn_hidden; s.B = c->batch; s.T = c->seq_len; s.N = s.B * s.T; s.tied = c->tied != 0;
+    s.ldV = (s.V + 3) / 4 * 4;
     s.P = s.V * s.d + s.L * (2 * s.d + 4 * s.d * s.d + 3 * s.F * s.d) + (s.tied ? 0 : s.V * s.d);
     return s;
 }
@@ -184,11 +186,14 @@ int64_t split_floats(const Sizes& s) {
     // per-chunk partials of the weight-gradient contractions over N tokens
     mlb::GemmPlan auto_plan;
     int64_t best = 0;
-    const int64_t shapes[6][3] = {{3 * s.d, s.d, s.N}, {s.d, s.d, s.N}, {2 * s.F, s.d, s.N},
-                                  {s.d, s.F, s.N},     {s.V, s.d, s.N}, {s.N, s.d, s.V}};
+    // {M, N, K, kseg} of every contraction of the step
+    const int64_t shapes[][4] = {{3 * s.d, s.d, s.N, s.N}, {s.d, s.d, s.N, s.N},    {2 * s.F, s.d, s.N, s.N},
+                                 {s.d, s.F, s.N, s.N},     {s.V, s.d, s.N, s.N},    {s.N, s.d, s.V, s.V},
+                                 {s.N, s.d, s.F, s.F},     {s.N, s.d, 2 * s.F, s.F}, {s.N, s.d, 3 * s.d, s.d},
+                                 {s.N, s.F, s.d, s.d},     {s.N, s.d, s.d, s.d}};
     for (const auto& sh : shapes) {
         mlb::GemmDesc g;
-        g.M = sh[0]; g.N = sh[1]; g.K = sh[2]; g.kseg = sh[2];
+        g.M = sh[0]; g.N = sh[1]; g.K = sh[2]; g.kseg = sh[3];
         int64_t f = mlb::gemm_split_scratch(g, auto_plan);
         if (f > best) best = f;
     }
@@ -271,7 +276,7 @@ size_t carve(mlb_model* M, char* base) {
         M->gu[l] = c.take<float>(s.N * 2 * s.F);
         M->a[l] = c.take<float>(s.N * s.F);
     }
-    M->logits = c.take<float>(s.N * s.V);
+    M->logits = c.take<float>(s.N * s.ldV);
     M->dh = c.take<float>(s.N * s.d);
     M->dA = c.take<float>(s.N * s.F);
     M->dgu = c.take<float>(s.N * 2 * s.F);
@@ -419,6 +424,26 @@ mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
         if (r_ != 0) return fail(MLB_E_DEVICE, "%s returned %d", #x, r_);            \
     } while (0)
 
+// Lower-triangle contraction over the head dimension for all B*H heads:
+// rows of A and B at stride ld (head h at column h*hd, batch b at b*sb).
+mlb_status run_tri(mlb_model* M, const char* site, int64_t T, int64_t hd, const float* A, int64_t lda, int64_t sAb,
+                   const float* B, int64_t ldb, int64_t sBb, float* C, int scaled, float scale) {
+    const Sizes& s = M->s;
+    const int64_t ev = stat_begin(M);
+    const int r = mlb::tri_nt(T, hd, s.B * s.H, s.H, A, lda, sAb, hd, B, ldb, sBb, hd, C, T, s.H * T * T, T * T,
+                              scaled, scale, M->stream);
+    stat_end(M, ev, site, "k_tri_nt", 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd,
+             0.0);
+    if (r != 0) return fail(MLB_E_DEVICE, "%s failed (%d)", site, r);
+    return MLB_OK;
+}
+
+#define TRI(site, ...)                                       \
+    do {                                                     \
+        mlb_status st_ = run_tri(M, site, __VA_ARGS__);      \
+        if (st_ != MLB_OK) return st_;                       \
+    } while (0)
+
 // Per-head attention contractions on [N, 3d] (q | k | v) and [N, d] rows.
 mlb::GemmDesc head_gemm(const Sizes& s) {
     mlb::GemmDesc g;
@@ -439,13 +464,9 @@ mlb_status forward(mlb_model* M) {
         RUN("qkv_fwd", lin(N, 3 * d, d, M->xn1[l], d, true, M->p + M->o_qkv[l], d, true, M->qkv[l], 3 * d, 0));
         OP("rope_fwd", f4 * 4 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
         OP("rope_fwd", f4 * 4 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
-        mlb::GemmDesc sg = head_gemm(s);   // S = (q . k) * scale, j <= i
-        sg.M = T; sg.N = T; sg.K = hd; sg.kseg = hd;
-        sg.A = M->qkv[l]; sg.lda = 3 * d; sg.a_kc = true; sg.sAb = T * 3 * d; sg.sAh = hd;
-        sg.B = M->qkv[l] + d; sg.ldb = 3 * d; sg.b_kc = true; sg.sBb = T * 3 * d; sg.sBh = hd;
-        sg.C = M->P[l]; sg.ldc = T; sg.sCb = H * T * T; sg.sCh = T * T;
-        sg.outmask = 1; sg.mode = 2; sg.scale = M->attn_scale;
-        RUN("attn_scores", sg);
+        // S = (q . k) * scale, j <= i
+        TRI("attn_scores", T, hd, M->qkv[l], 3 * d, T * 3 * d, M->qkv[l] + d, 3 * d, T * 3 * d, M->P[l], 1,
+            M->attn_scale);
         OP("softmax_fwd", f4 * 2 * tri, mlb::softmax_causal(M->P[l], BH, T, st));
         mlb::GemmDesc pv = head_gemm(s);   // O = P v over j <= i
         pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.krange = 1;
@@ -464,8 +485,9 @@ mlb_status forward(mlb_model* M) {
         wd.R = M->hmid[l];                 // h' = hmid + a Wd^T
         RUN("down_fwd", wd);
     }
-    RUN("head_fwd", lin(N, s.V, d, M->h[s.L], d, true, M->p + M->offOut, d, true, M->logits, s.V, 0));
-    OP("xent", f4 * 2 * N * s.V, mlb::cross_entropy(M->logits, M->tg, N, s.V, M->loss_rows, M->logits, M->err, st));
+    RUN("head_fwd", lin(N, s.V, d, M->h[s.L], d, true, M->p + M->offOut, d, true, M->logits, s.ldV, 0));
+    OP("xent", f4 * 2 * N * s.V,
+       mlb::cross_entropy(M->logits, M->tg, N, s.V, s.ldV, M->loss_rows, M->logits, M->err, st));
     OP("loss_sum", f4 * N, mlb::sum64_scaled(M->loss_rows, N, M->invN, M->loss_dev, st));
     return MLB_OK;
 }
@@ -477,9 +499,9 @@ mlb_status backward(mlb_model* M) {
     const double f4 = 4.0, tri = (double)BH * (double)T * (double)(T + 1) / 2.0;
     const float* dl = M->logits;
     // head: dh = dl W_out (K = V); W_out gradient = dl^T h_L (K = N), folded into G
-    RUN("head_dx", lin(N, d, s.V, dl, s.V, true, M->p + M->offOut, d, false, M->dh, d, 0));
-    if (s.tied) RUN("head_dw", lin(s.V, d, N, dl, s.V, false, M->h[s.L], d, false, M->gE, d, 0));
-    else RUN("head_dw", lin(s.V, d, N, dl, s.V, false, M->h[s.L], d, false, M->G + M->offOut, d, 1));
+    RUN("head_dx", lin(N, d, s.V, dl, s.ldV, true, M->p + M->offOut, d, false, M->dh, d, 0));
+    if (s.tied) RUN("head_dw", lin(s.V, d, N, dl, s.ldV, false, M->h[s.L], d, false, M->gE, d, 0));
+    else RUN("head_dw", lin(s.V, d, N, dl, s.ldV, false, M->h[s.L], d, false, M->G + M->offOut, d, 1));
     for (int64_t l = s.L - 1; l >= 0; --l) {
         // MLP branch
         RUN("down_dx", lin(N, F, d, M->dh, d, true, M->p + M->o_wd[l], F, false, M->dA, F, 0));
@@ -497,12 +519,8 @@ mlb_status backward(mlb_model* M) {
         RUN("wo_dx", lin(N, d, d, M->dh, d, true, M->p + M->o_wo[l], d, false, M->dO, d, 0));
         RUN("wo_dw", lin(d, d, N, M->dh, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
         OP("attn_rowdot", f4 * (2 * N * d + BH * T), mlb::attn_rowdot(M->dO, M->O[l], s.B, H, T, hd, d, M->Dv, st));
-        mlb::GemmDesc dp = head_gemm(s);   // dP = dO . v, j <= i
-        dp.M = T; dp.N = T; dp.K = hd; dp.kseg = hd; dp.outmask = 1;
-        dp.A = M->dO; dp.lda = d; dp.a_kc = true; dp.sAb = T * d; dp.sAh = hd;
-        dp.B = M->qkv[l] + 2 * d; dp.ldb = 3 * d; dp.b_kc = true; dp.sBb = T * 3 * d; dp.sBh = hd;
-        dp.C = M->dP; dp.ldc = T; dp.sCb = H * T * T; dp.sCh = T * T;
-        RUN("attn_dp", dp);
+        // dP = dO . v, j <= i
+        TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f);
         mlb::GemmDesc dv = head_gemm(s);   // dv = P^T dO over i >= j
         dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.krange = 2;
         dv.A = M->P[l]; dv.lda = T; dv.a_kc = false; dv.sAb = H * T * T; dv.sAh = T * T;
@@ -800,7 +818,7 @@ mlb_status mlb_read_stage(const mlb_model* M, int stage, int layer, void* dst, s
         case 9: src = M->gu[layer]; n = s.N * 2 * s.F; break;
         case 10: src = M->a[layer]; n = s.N * s.F; break;
         case 11: src = M->h[s.L]; n = s.N * s.d; break;
-        case 12: src = M->logits; n = s.N * s.V; break;
+        case 12: src = M->logits; n = s.N * s.V; break;   // rows compacted from the padded stride
         case 13: src = M->loss_rows; n = s.N; break;
         default: return fail(MLB_E_INVALID_ARG, "unknown stage %d", stage);
     }
@@ -809,7 +827,11 @@ mlb_status mlb_read_stage(const mlb_model* M, int stage, int layer, void* dst, s
     if (bytes < (size_t)n * 4) return fail(MLB_E_IO, "buffer too small");
     HIPCHK(hipSetDevice(M->device));
     HIPCHK(hipStreamSynchronize(M->stream));
-    HIPCHK(hipMemcpy(dst, src, (size_t)n * 4, hipMemcpyDeviceToHost));
+    if (stage == 12)
+        HIPCHK(hipMemcpy2D(dst, (size_t)s.V * 4, src, (size_t)s.ldV * 4, (size_t)s.V * 4, (size_t)s.N,
+                           hipMemcpyDeviceToHost));
+    else
+        HIPCHK(hipMemcpy(dst, src, (size_t)n * 4, hipMemcpyDeviceToHost));
     return MLB_OK;
 }
 
@@ -889,7 +911,7 @@ mlb_status mlb_prim_gemm(int64_t M, int64_t N, int64_t K, int64_t kseg, const fl
     g.A = A; g.lda = lda; g.a_kc = a_kc != 0; g.B = B; g.ldb = ldb; g.b_kc = b_kc != 0; g.C = C; g.ldc = ldc;
     g.krange = krange; g.outmask = outmask; g.mode = mode; g.scale = scale;
     g.batch = batch; g.H = heads; g.sAb = sAb; g.sAh = sAh; g.sBb = sBb; g.sBh = sBh; g.sCb = sCb; g.sCh = sCh;
-    if (tile < -1 || tile > 1) return fail(MLB_E_INVALID_ARG, "tile %d", tile);
+    if (tile < -1 || tile > 2) return fail(MLB_E_INVALID_ARG, "tile %d", tile);
     mlb::GemmPlan p;
     p.tile = tile; p.split = split; p.simple = simple;
     p.scratch = static_cast<float*>(ws);
@@ -943,14 +965,20 @@ mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     if (!q || !k || !v || !P || !O || B <= 0 || H <= 0 || T <= 0 || hd <= 0) return fail(MLB_E_INVALID_ARG, "attention");
     hipStream_t st = static_cast<hipStream_t>(stream);
     mlb::GemmPlan plan;
-    mlb::GemmDesc sg;
-    sg.batch = B * H; sg.H = H;
-    sg.M = T; sg.N = T; sg.K = hd; sg.kseg = hd;
-    sg.A = q; sg.lda = ld; sg.a_kc = true; sg.sAb = T * ld; sg.sAh = hd;
-    sg.B = k; sg.ldb = ld; sg.b_kc = true; sg.sBb = T * ld; sg.sBh = hd;
-    sg.C = P; sg.ldc = T; sg.sCb = H * T * T; sg.sCh = T * T;
-    sg.outmask = 1; sg.mode = 2; sg.scale = (float)(1.0 / std::sqrt((double)hd));
-    if (mlb::gemm(sg, plan, st)) return fail(MLB_E_DEVICE, "scores");
+    const float scale = (float)(1.0 / std::sqrt((double)hd));
+    if (hd <= 64) {
+        if (mlb::tri_nt(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T, H * T * T, T * T, 1, scale, st))
+            return fail(MLB_E_DEVICE, "scores");
+    } else {
+        mlb::GemmDesc sg;
+        sg.batch = B * H; sg.H = H;
+        sg.M = T; sg.N = T; sg.K = hd; sg.kseg = hd;
+        sg.A = q; sg.lda = ld; sg.a_kc = true; sg.sAb = T * ld; sg.sAh = hd;
+        sg.B = k; sg.ldb = ld; sg.b_kc = true; sg.sBb = T * ld; sg.sBh = hd;
+        sg.C = P; sg.ldc = T; sg.sCb = H * T * T; sg.sCh = T * T;
+        sg.outmask = 1; sg.mode = 2; sg.scale = scale;
+        if (mlb::gemm(sg, plan, st)) return fail(MLB_E_DEVICE, "scores");
+    }
     if (mlb::softmax_causal(P, B * H, T, st)) return fail(MLB_E_DEVICE, "softmax");
     mlb::GemmDesc pv;
     pv.batch = B * H; pv.H = H;
@@ -976,13 +1004,18 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     mlb::GemmPlan plan;
     const float scale = (float)(1.0 / std::sqrt((double)hd));
     if (mlb::attn_rowdot(dO, O, B, H, T, hd, ldo, D, st)) return fail(MLB_E_DEVICE, "rowdot");
-    mlb::GemmDesc g;
-    g.batch = B * H; g.H = H;
-    g.M = T; g.N = T; g.K = hd; g.kseg = hd; g.outmask = 1;
-    g.A = dO; g.lda = ldo; g.a_kc = true; g.sAb = T * ldo; g.sAh = hd;
-    g.B = v; g.ldb = ld; g.b_kc = true; g.sBb = T * ld; g.sBh = hd;
-    g.C = dP; g.ldc = T; g.sCb = H * T * T; g.sCh = T * T;
-    if (mlb::gemm(g, plan, st)) return fail(MLB_E_DEVICE, "dP");
+    if (hd <= 64) {
+        if (mlb::tri_nt(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T, H * T * T, T * T, 0, 1.0f, st))
+            return fail(MLB_E_DEVICE, "dP");
+    } else {
+        mlb::GemmDesc g;
+        g.batch = B * H; g.H = H;
+        g.M = T; g.N = T; g.K = hd; g.kseg = hd; g.outmask = 1;
+        g.A = dO; g.lda = ldo; g.a_kc = true; g.sAb = T * ldo; g.sAh = hd;
+        g.B = v; g.ldb = ld; g.b_kc = true; g.sBb = T * ld; g.sBh = hd;
+        g.C = dP; g.ldc = T; g.sCb = H * T * T; g.sCh = T * T;
+        if (mlb::gemm(g, plan, st)) return fail(MLB_E_DEVICE, "dP");
+    }
     mlb::GemmDesc gv;
     gv.batch = B * H; gv.H = H;
     gv.M = T; gv.N = hd; gv.K = T; gv.kseg = T; gv.krange = 2;
@@ -1028,7 +1061,7 @@ mlb_status mlb_prim_cross_entropy(const float* logits, const int32_t* targets, i
     int* err = nullptr;
     HIPCHK(hipMalloc(reinterpret_cast<void**>(&err), 4));
     HIPCHK(hipMemsetAsync(err, 0, 4, st));
-    const int r = mlb::cross_entropy(logits, targets, N, V, loss_rows, dl, err, st);
+    const int r = mlb::cross_entropy(logits, targets, N, V, V, loss_rows, dl, err, st);
     const int r2 = r == 0 ? mlb::sum64_scaled(loss_rows, N, 1.0f / (float)N, loss_dev, st) : r;
     int herr = 0;
     HIPCHK(hipMemcpyAsync(&herr, err, 4, hipMemcpyDeviceToHost, st));

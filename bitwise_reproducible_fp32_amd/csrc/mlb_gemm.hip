@@ -58,9 +58,12 @@ __device__ __forceinline__ void epilogue_store(const KArgs& a, float* C, int64_t
     else *p = a.R[gi * a.ldc + gj] + v;
 }
 
-template <bool AKC, bool BKC, int WM, int WN, int KR, bool VEC>
+template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, bool VEC, bool MC>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
-    constexpr int MT = 64 * WM, NT = 64 * WN, NTHR = 64 * WM * WN;
+    // Each wave owns RB 32-row blocks x 64 columns (two 32x32 MFMA blocks per
+    // row block). MC: the contraction may span several 1024-chunks, so a
+    // running total is kept beside the chunk accumulator.
+    constexpr int MT = 32 * RB * WM, NT = 64 * WN, NTHR = 64 * WM * WN;
     constexpr int ALD = AKC ? KT + 1 : MT + 4;
     constexpr int BLD = BKC ? KT + 1 : NT + 4;
     constexpr int ASZ = AKC ? MT * ALD : KT * ALD;
@@ -74,6 +77,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % WM, wn = wave / WM;
+    const int lk = lane >> 5, li = lane & 31;
 
     // XCD-aware tile order, then grouped rows.
     const int64_t w = blockIdx.x, nt = a.ntiles;
@@ -85,7 +89,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     const int64_t gsize = (a.tiles_m - first_m) < GM ? (a.tiles_m - first_m) : GM;
     const int64_t tm = first_m + (logical % per_group) % gsize;
     const int64_t tn = (logical % per_group) / gsize;
-    const int64_t i0 = tm * MT, j0 = tn * NT;
+    // k <= i: later row tiles hold more work, so they are dispatched first
+    const int64_t tmr = (KR == 1) ? a.tiles_m - 1 - tm : tm;
+    const int64_t i0 = tmr * MT, j0 = tn * NT;
     if (a.outmask && j0 > i0 + MT - 1) return;   // whole tile above the diagonal: nothing to write
 
     const int64_t z = blockIdx.z, zb = z / a.H, zh = z % a.H;
@@ -94,22 +100,25 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     float* C = a.C + zb * a.sCb + zh * a.sCh;
 
     int64_t kbeg = 0, kend = a.K;
-    if (a.split) { kbeg = (int64_t)blockIdx.y * KC; kend = (kbeg + KC < a.K) ? kbeg + KC : a.K; }
+    if (a.split) {   // one chunk of the segment-major chunk list
+        const int64_t per_seg = (a.kseg + KC - 1) / KC;
+        const int64_t sg = (int64_t)blockIdx.y / per_seg, ch = (int64_t)blockIdx.y % per_seg;
+        kbeg = sg * a.kseg + ch * KC;
+        kend = sg * a.kseg + ((ch + 1) * KC < a.kseg ? (ch + 1) * KC : a.kseg);
+    }
     if (KR == 1) kend = (kend < i0 + MT) ? kend : i0 + MT;
     if (KR == 2) kbeg = (kbeg > i0) ? kbeg : i0;
     const int64_t kt0 = kbeg / KT, kt1 = (kend + KT - 1) / KT;
 
-    v16f acc[2][2], tot[2][2];
+    v16f acc00, acc01, acc10, acc11, tot00, tot01, tot10, tot11;
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) { acc[r][c][e] = 0.0f; tot[r][c][e] = 0.0f; }
-    bool have[2] = {false, false}, dirty[2] = {false, false};
-    int64_t bi0[2];
-    bi0[0] = i0 + wm * 64;
-    bi0[1] = bi0[0] + 32;
+    for (int e = 0; e < 16; ++e) {
+        acc00[e] = 0.0f; acc01[e] = 0.0f; acc10[e] = 0.0f; acc11[e] = 0.0f;
+        tot00[e] = 0.0f; tot01[e] = 0.0f; tot10[e] = 0.0f; tot11[e] = 0.0f;
+    }
+    bool have0 = false, have1 = false, dirty0 = false, dirty1 = false;
+    const int r0 = wm * 32 * RB, r1 = r0 + 32;            // row offsets of the wave's blocks in the tile
+    const int64_t bi00 = i0 + r0, bi01 = i0 + r1;
 
     float ra[EA * W], rb[EB * W];
     auto load_global = [&](int64_t kt) {
@@ -121,10 +130,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
             if (AKC) { gi = i0 + q / (KT / W); gk = k0 + (q % (KT / W)) * W; }
             else { gk = k0 + q / (MT / W); gi = i0 + (q % (MT / W)) * W; }
             if (VEC) {
+                // the leading dimension covers the vector past the last element;
+                // positions past K read as -0, rows past M as 0
                 if (gk < a.K && gi < a.M) {
                     const float4 v = AKC ? *reinterpret_cast<const float4*>(A + gi * a.lda + gk)
                                          : *reinterpret_cast<const float4*>(A + gk * a.lda + gi);
                     ra[s * 4 + 0] = v.x; ra[s * 4 + 1] = v.y; ra[s * 4 + 2] = v.z; ra[s * 4 + 3] = v.w;
+                    if (AKC) {
+#pragma unroll
+                        for (int e = 1; e < 4; ++e) if (gk + e >= a.K) ra[s * 4 + e] = -0.0f;
+                    }
                 } else {
                     const float f = (gk >= a.K) ? -0.0f : 0.0f;
                     ra[s * 4 + 0] = f; ra[s * 4 + 1] = f; ra[s * 4 + 2] = f; ra[s * 4 + 3] = f;
@@ -146,6 +161,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
                     const float4 v = BKC ? *reinterpret_cast<const float4*>(B + gj * a.ldb + gk)
                                          : *reinterpret_cast<const float4*>(B + gk * a.ldb + gj);
                     rb[s * 4 + 0] = v.x; rb[s * 4 + 1] = v.y; rb[s * 4 + 2] = v.z; rb[s * 4 + 3] = v.w;
+                    if (BKC) {
+#pragma unroll
+                        for (int e = 1; e < 4; ++e) if (gk + e >= a.K) rb[s * 4 + e] = 0.0f;
+                    }
                 } else {
                     rb[s * 4 + 0] = 0.0f; rb[s * 4 + 1] = 0.0f; rb[s * 4 + 2] = 0.0f; rb[s * 4 + 3] = 0.0f;
                 }
@@ -185,17 +204,60 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     };
     auto a_lds = [&](int i, int k) -> float { return AKC ? As[i * ALD + k] : As[k * ALD + i]; };
     auto b_lds = [&](int k, int j) -> float { return BKC ? Bs[j * BLD + k] : Bs[k * BLD + j]; };
-    auto fold = [&](int r) {
-        if (!dirty[r]) return;
+    auto fold_pair = [&](v16f& t0, v16f& t1, v16f& c0, v16f& c1, bool& have, bool& dirty) {
+        if (!dirty) return;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int e = 0; e < 16; ++e) {
+            t0[e] = have ? t0[e] + c0[e] : c0[e];
+            t1[e] = have ? t1[e] + c1[e] : c1[e];
+            c0[e] = 0.0f;
+            c1[e] = 0.0f;
+        }
+        have = true;
+        dirty = false;
+    };
+    const int j0l = wn * 64 + li, j1l = j0l + 32;
+    // one 32-row block against the wave's two 32-column blocks, all 16 k-pairs
+    auto full_block = [&](v16f& c0, v16f& c1, int rloc) {
+#pragma unroll 4
+        for (int p = 0; p < KT / 2; ++p) {
+            const int kk = 2 * p + lk;
+            const float av = a_lds(rloc + li, kk);
+            const float b0 = b_lds(kk, j0l), b1 = b_lds(kk, j1l);
+            c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, c1, 0, 0, 0);
+        }
+    };
+    // The tile on the diagonal (k0 equals the block's first row). Row il of
+    // the block has its causal range boundary inside the tile. For each k-pair
+    // (ka, kb) = (2p, 2p+1) the pair's MFMA result is kept for rows that take
+    // both terms (k <= i: il >= kb; k >= i: il <= ka); the one row whose range
+    // boundary falls between them (il == ka, resp. il == kb) takes the single
+    // term with one fma; every other row keeps its value. Positions past K are
+    // padded (-0 * +0) and change nothing.
+    auto diag_block = [&](v16f& c0, v16f& c1, int rloc) {
+#pragma unroll 1
+        for (int p = 0; p < KT / 2; ++p) {
+            const int kk = 2 * p + lk;
+            const float av = a_lds(rloc + li, kk);
+            const float b0 = b_lds(kk, j0l), b1 = b_lds(kk, j1l);
+            const v16f n0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, c0, 0, 0, 0);
+            const v16f n1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, c1, 0, 0, 0);
+            const int ka = 2 * p, kb = 2 * p + 1;
+            const int ks = (KR == 1) ? ka : kb;               // the single term's k, also its row
+            const float as = a_lds(rloc + ks, ks);
+            const float bs0 = b_lds(ks, j0l), bs1 = b_lds(ks, j1l);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                tot[r][c][e] = have[r] ? tot[r][c][e] + acc[r][c][e] : acc[r][c][e];
-                acc[r][c][e] = 0.0f;
+                const int il = 8 * (e >> 2) + 4 * lk + (e & 3);
+                const bool both = (KR == 1) ? (il >= kb) : (il <= ka);
+                const bool single = (il == ks);
+                const float s0 = __builtin_fmaf(as, bs0, c0[e]);
+                const float s1 = __builtin_fmaf(as, bs1, c1[e]);
+                c0[e] = both ? n0[e] : (single ? s0 : c0[e]);
+                c1[e] = both ? n1[e] : (single ? s1 : c1[e]);
             }
-        have[r] = true;
-        dirty[r] = false;
+        }
     };
 
     int64_t prev_chunk = -1;
@@ -206,97 +268,78 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
         store_lds();
         __syncthreads();
         if (kt + 1 < kt1) load_global(kt + 1);
-        const int64_t chunk = (k0 / a.kseg) * (a.kseg / KC + 1) + (k0 % a.kseg) / KC;
-        if (chunk != prev_chunk) {
-            if (prev_chunk >= 0 && !a.split) { fold(0); fold(1); }
-            prev_chunk = chunk;
+        if (MC) {
+            const int64_t chunk = (k0 / a.kseg) * (a.kseg / KC + 1) + (k0 % a.kseg) / KC;
+            if (chunk != prev_chunk) {
+                if (prev_chunk >= 0) {
+                    fold_pair(tot00, tot01, acc00, acc01, have0, dirty0);
+                    if (RB == 2) fold_pair(tot10, tot11, acc10, acc11, have1, dirty1);
+                }
+                prev_chunk = chunk;
+            }
         }
-        // per row-block: 0 skip, 1 full tile on the matrix cores, 2 diagonal tile on the VALU
-        int st[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (KR == 0) st[r] = 1;
-            else if (KR == 1) st[r] = (k0 < bi0[r]) ? 1 : (k0 == bi0[r] ? 2 : 0);
-            else st[r] = (k0 > bi0[r]) ? 1 : (k0 == bi0[r] ? 2 : 0);
-            if (st[r]) dirty[r] = true;
+        // per row block: 0 skip, 1 full tile, 2 diagonal tile
+        int st0 = 1, st1 = 1;
+        if (KR == 1) {
+            st0 = (k0 < bi00) ? 1 : (k0 == bi00 ? 2 : 0);
+            st1 = (k0 < bi01) ? 1 : (k0 == bi01 ? 2 : 0);
+        } else if (KR == 2) {
+            st0 = (k0 > bi00) ? 1 : (k0 == bi00 ? 2 : 0);
+            st1 = (k0 > bi01) ? 1 : (k0 == bi01 ? 2 : 0);
         }
-        const int lk = lane >> 5, li = lane & 31;
-        if (st[0] == 1 && st[1] == 1) {
+        dirty0 = dirty0 || st0 != 0;
+        dirty1 = dirty1 || st1 != 0;
+        if (RB == 2 && st0 == 1 && st1 == 1) {
 #pragma unroll 4
             for (int p = 0; p < KT / 2; ++p) {
                 const int kk = 2 * p + lk;
-                const float a0 = a_lds(wm * 64 + li, kk);
-                const float a1 = a_lds(wm * 64 + 32 + li, kk);
-                const float b0 = b_lds(kk, wn * 64 + li);
-                const float b1 = b_lds(kk, wn * 64 + 32 + li);
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+                const float a0 = a_lds(r0 + li, kk);
+                const float a1 = a_lds(r1 + li, kk);
+                const float b0 = b_lds(kk, j0l);
+                const float b1 = b_lds(kk, j1l);
+                acc00 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc00, 0, 0, 0);
+                acc01 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc01, 0, 0, 0);
+                acc10 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc10, 0, 0, 0);
+                acc11 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc11, 0, 0, 0);
             }
-        } else if (KR != 0) {
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                if (st[r] == 1) {
-                    for (int p = 0; p < KT / 2; ++p) {
-                        const int kk = 2 * p + lk;
-                        const float av = a_lds(wm * 64 + r * 32 + li, kk);
-                        const float b0 = b_lds(kk, wn * 64 + li);
-                        const float b1 = b_lds(kk, wn * 64 + 32 + li);
-                        acc[r][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, acc[r][0], 0, 0, 0);
-                        acc[r][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, acc[r][1], 0, 0, 0);
-                    }
-                } else if (st[r] == 2) {
-                    // per-element chains over this tile's 32 k in ascending order
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const int jl = wn * 64 + c * 32 + li;
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int il = wm * 64 + r * 32 + 8 * (e >> 2) + 4 * lk + (e & 3);
-                            const int64_t gi = i0 + il;
-                            float v = acc[r][c][e];
-                            for (int kk = 0; kk < KT; ++kk) {
-                                const int64_t gk = k0 + kk;
-                                const bool ok = (KR == 1 ? gk <= gi : gk >= gi) && gk < a.K;
-                                if (ok) v = __builtin_fmaf(a_lds(il, kk), b_lds(kk, jl), v);
-                            }
-                            acc[r][c][e] = v;
-                        }
-                    }
-                }
+        } else {
+            if (st0 == 1) full_block(acc00, acc01, r0);
+            else if (KR != 0 && st0 == 2) diag_block(acc00, acc01, r0);
+            if (RB == 2) {
+                if (st1 == 1) full_block(acc10, acc11, r1);
+                else if (KR != 0 && st1 == 2) diag_block(acc10, acc11, r1);
             }
         }
     }
 
-    const int lk = lane >> 5, li = lane & 31;
-    if (a.split) {
-        float* part = a.part + (int64_t)blockIdx.y * a.M * a.N;
+    auto store_pair = [&](const v16f& v0, const v16f& v1, int64_t bi, bool valid) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t gi = bi0[r] + 8 * (e >> 2) + 4 * lk + (e & 3);
-                    const int64_t gj = j0 + wn * 64 + c * 32 + li;
-                    if (gi < a.M && gj < a.N) part[gi * a.N + gj] = acc[r][c][e];
-                }
-        return;
-    }
-    fold(0);
-    fold(1);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t gi = bi0[r] + 8 * (e >> 2) + 4 * lk + (e & 3);
-                const int64_t gj = j0 + wn * 64 + c * 32 + li;
-                if (gi < a.M && gj < a.N && (!a.outmask || gj <= gi))
-                    epilogue_store(a, C, gi, gj, have[r] ? tot[r][c][e] : 0.0f);
+        for (int e = 0; e < 16; ++e) {
+            const int64_t gi = bi + 8 * (e >> 2) + 4 * lk + (e & 3);
+            const int64_t gj0 = j0 + j0l, gj1 = j0 + j1l;
+            if (a.split) {
+                float* part = a.part + (int64_t)blockIdx.y * a.M * a.N;
+                if (gi < a.M && gj0 < a.N) part[gi * a.N + gj0] = v0[e];
+                if (gi < a.M && gj1 < a.N) part[gi * a.N + gj1] = v1[e];
+            } else {
+                if (gi < a.M && gj0 < a.N && (!a.outmask || gj0 <= gi))
+                    epilogue_store(a, C, gi, gj0, valid ? v0[e] : 0.0f);
+                if (gi < a.M && gj1 < a.N && (!a.outmask || gj1 <= gi))
+                    epilogue_store(a, C, gi, gj1, valid ? v1[e] : 0.0f);
             }
+        }
+    };
+    if (MC && !a.split) {
+        fold_pair(tot00, tot01, acc00, acc01, have0, dirty0);
+        store_pair(tot00, tot01, bi00, have0);
+        if (RB == 2) {
+            fold_pair(tot10, tot11, acc10, acc11, have1, dirty1);
+            store_pair(tot10, tot11, bi01, have1);
+        }
+    } else {
+        store_pair(acc00, acc01, bi00, dirty0 || a.split);
+        if (RB == 2) store_pair(acc10, acc11, bi01, dirty1 || a.split);
+    }
 }
 
 // One thread per output, global loads, the chunk rule written out directly.
@@ -350,41 +393,47 @@ struct Cfg { int wm, wn; };
 
 thread_local char g_launched[96];
 
-template <bool AKC, bool BKC, int WM, int WN, int KR>
-void launch_t(const KArgs& a, bool vec, dim3 grid, hipStream_t s) {
-    std::snprintf(g_launched, sizeof g_launched, "k_gemm<%s, %s, %d, %d, %d, %s>", AKC ? "true" : "false",
-                  BKC ? "true" : "false", WM, WN, KR, vec ? "true" : "false");
-    if (vec) k_gemm<AKC, BKC, WM, WN, KR, true><<<grid, 64 * WM * WN, 0, s>>>(a);
-    else k_gemm<AKC, BKC, WM, WN, KR, false><<<grid, 64 * WM * WN, 0, s>>>(a);
+template <bool AKC, bool BKC, int WM, int WN, int RB, int KR>
+void launch_t(const KArgs& a, bool vec, bool mc, dim3 grid, hipStream_t s) {
+    std::snprintf(g_launched, sizeof g_launched, "k_gemm<%s, %s, %d, %d, %d, %d, %s, %s>", AKC ? "true" : "false",
+                  BKC ? "true" : "false", WM, WN, RB, KR, vec ? "true" : "false", (KR != 0 || mc) ? "true" : "false");
+    if (KR != 0 || mc) {
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, true><<<grid, 64 * WM * WN, 0, s>>>(a);
+        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, true><<<grid, 64 * WM * WN, 0, s>>>(a);
+    } else {
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, 0, true, false><<<grid, 64 * WM * WN, 0, s>>>(a);
+        else k_gemm<AKC, BKC, WM, WN, RB, 0, false, false><<<grid, 64 * WM * WN, 0, s>>>(a);
+    }
 }
 
+// Tile configurations: 0 = 128x128 (2x2 waves of 64x64), 1 = 256x64 (4x1 waves
+// of 64x64), 2 = 128x64 (4x1 waves of 32x64; the causal ranges).
 // Returns false when no tiled instantiation exists for the combination.
-bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, int64_t nsplit, hipStream_t s) {
-    const int WM = cfg == 0 ? 2 : 4, WN = cfg == 0 ? 2 : 1;
-    a.tiles_m = (d.M + 64 * WM - 1) / (64 * WM);
-    a.tiles_n = (d.N + 64 * WN - 1) / (64 * WN);
+bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_t nsplit, hipStream_t s) {
+    const int64_t MT = cfg == 0 ? 128 : (cfg == 1 ? 256 : 128), NT = cfg == 0 ? 128 : 64;
+    a.tiles_m = (d.M + MT - 1) / MT;
+    a.tiles_n = (d.N + NT - 1) / NT;
     a.ntiles = a.tiles_m * a.tiles_n;
     const dim3 grid((unsigned)a.ntiles, (unsigned)nsplit, (unsigned)d.batch);
     const int key = (d.a_kc ? 1 : 0) | (d.b_kc ? 2 : 0);
-    if (d.krange == 0) {
-        if (cfg == 0) {
-            switch (key) {
-                case 3: launch_t<true, true, 2, 2, 0>(a, vec, grid, s); return true;
-                case 1: launch_t<true, false, 2, 2, 0>(a, vec, grid, s); return true;
-                case 0: launch_t<false, false, 2, 2, 0>(a, vec, grid, s); return true;
-                case 2: launch_t<false, true, 2, 2, 0>(a, vec, grid, s); return true;
-            }
-        } else {
-            switch (key) {
-                case 3: launch_t<true, true, 4, 1, 0>(a, vec, grid, s); return true;
-                case 1: launch_t<true, false, 4, 1, 0>(a, vec, grid, s); return true;
-                case 0: launch_t<false, false, 4, 1, 0>(a, vec, grid, s); return true;
-                case 2: launch_t<false, true, 4, 1, 0>(a, vec, grid, s); return true;
-            }
+    if (d.krange == 0 && cfg == 0) {
+        switch (key) {
+            case 3: launch_t<true, true, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
+            case 1: launch_t<true, false, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
+            case 0: launch_t<false, false, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
+            case 2: launch_t<false, true, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
         }
     }
-    if (d.krange == 1 && key == 1 && cfg == 1) { launch_t<true, false, 4, 1, 1>(a, vec, grid, s); return true; }
-    if (d.krange == 2 && key == 0 && cfg == 1) { launch_t<false, false, 4, 1, 2>(a, vec, grid, s); return true; }
+    if (d.krange == 0 && cfg == 1) {
+        switch (key) {
+            case 3: launch_t<true, true, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
+            case 1: launch_t<true, false, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
+            case 0: launch_t<false, false, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
+            case 2: launch_t<false, true, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
+        }
+    }
+    if (d.krange == 1 && key == 1 && cfg == 2) { launch_t<true, false, 4, 1, 1, 1>(a, vec, mc, grid, s); return true; }
+    if (d.krange == 2 && key == 0 && cfg == 2) { launch_t<false, false, 4, 1, 1, 2>(a, vec, mc, grid, s); return true; }
     return false;
 }
 
@@ -402,15 +451,21 @@ static bool desc_ok(const GemmDesc& d) {
     return true;
 }
 
-static int64_t nchunks(const GemmDesc& d) { return d.K > 0 ? (d.K + KC - 1) / KC : 0; }
+// Number of chunks in the segment-major chunk list.
+static int64_t nchunks(const GemmDesc& d) {
+    if (d.K <= 0 || d.kseg <= 0) return 0;
+    return (d.K / d.kseg) * ((d.kseg + KC - 1) / KC);
+}
 
 // Whether per-chunk partials are worth it: only when the output has too few
 // tiles to fill the chip. Never changes bits.
+// Whether per-chunk partials (folded by a second kernel) are worth it: when
+// the output has too few tiles to fill the chip, or when several chunks would
+// otherwise need the running-total registers. Never changes bits.
 static bool split_useful(const GemmDesc& d, const GemmPlan& p) {
-    if (p.split == 0 || d.krange != 0 || d.batch != 1 || d.outmask || d.K <= KC || d.K != d.kseg) return false;
+    if (p.split == 0 || d.krange != 0 || d.batch != 1 || d.outmask || nchunks(d) < 2) return false;
     if (p.split == 1) return true;
-    const int64_t tiles = ((d.M + 127) / 128) * ((d.N + 127) / 128);
-    return tiles < 512;
+    return nchunks(d) <= 64;
 }
 
 static bool want_split(const GemmDesc& d, const GemmPlan& p) {
@@ -443,10 +498,15 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s) {
         k_gemm_simple<<<grid, 256, 0, s>>>(a, d.a_kc ? 1 : 0, d.b_kc ? 1 : 0);
         return hipGetLastError() == hipSuccess ? 0 : -3;
     }
+    // float4 loads need 16-byte alignment and a leading dimension that covers
+    // the contiguous extent rounded up to 4 (the slack is read, then masked)
+    auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
     bool vec = aligned16(d.A) && aligned16(d.B) && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
                d.sAb % 4 == 0 && d.sAh % 4 == 0 && d.sBb % 4 == 0 && d.sBh % 4 == 0;
-    vec = vec && (d.a_kc ? d.K % 4 == 0 : d.M % 4 == 0) && (d.b_kc ? d.K % 4 == 0 : d.N % 4 == 0);
-    int cfg = p.tile >= 0 ? p.tile : (d.N <= 64 ? 1 : 0);
+    vec = vec && (d.a_kc ? up4(d.K) <= d.lda : up4(d.M) <= d.lda) && (d.b_kc ? up4(d.K) <= d.ldb : up4(d.N) <= d.ldb);
+    // 128x128 tiles in general, 256x64 for 64-wide outputs, one-wave 64x64 tiles
+    // for causal ranges (their work per row tile grows along the diagonal)
+    int cfg = p.tile >= 0 ? p.tile : (d.krange != 0 ? 2 : (d.N <= 64 ? 1 : 0));
     const bool split = want_split(d, p);
     int64_t nsplit = 1;
     if (split) {
@@ -455,7 +515,9 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s) {
         a.split = 1;
         a.part = p.scratch;
     }
-    if (!launch_tiled(d, a, cfg, vec, nsplit, s)) {
+    // several chunks (or segments) per workgroup need the running total
+    const bool mc = !split && nchunks(d) > 1;
+    if (!launch_tiled(d, a, cfg, vec, mc, nsplit, s)) {
         if (split) return -1;
         const int64_t n = d.M * d.N;
         const dim3 grid((unsigned)((n + 255) / 256), 1, (unsigned)d.batch);

@@ -48,6 +48,13 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s);
 // (the split path also launches k_fold).
 const char* gemm_last_kernel();
 
+// Lower triangle of a batched contraction over a short K (<= 64, one chunk):
+// C(i,j) = t(i,j) (times scale when scaled) for j <= i < T, with
+// t(i,j) = fma chain over k of A[i*lda + k] * B[j*ldb + k] (mlb_attn.hip).
+int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
+           const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
+           int scaled, float scale, hipStream_t s);
+
 // Row and elementwise kernels (mlb_ops.hip). All return 0 or a negative value
 // on invalid sizes; they launch on stream s and never synchronise.
 int gather_rows(const int32_t* ids, const float* table, int64_t V, int64_t d, int64_t N, float* out,
@@ -73,8 +80,9 @@ int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t 
                 hipStream_t s);
 int swiglu_fwd(const float* gu, int64_t rows, int64_t F, float* a, hipStream_t s);
 int swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float* dgu, hipStream_t s);
-// Cross-entropy rows: loss_rows written, dl written (may alias logits).
-int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, float* loss_rows,
+// Cross-entropy rows (row stride ld >= V): loss_rows written, dl written
+// (may alias logits).
+int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, int64_t ld, float* loss_rows,
                   float* dl, int* err, hipStream_t s);
 // out[0] = SUM64(v[0..n)) * mul.
 int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s);

@@ -80,17 +80,32 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict_
 }
 
 // Gain gradient partials: part[ch][c] = fma chain over rows n of chunk ch
-// (1024 rows) of dy[n,c] * (x[n,c] * r[n]), from +0 in ascending n.
-__global__ __launch_bounds__(256) void k_rmsnorm_dw_part(const float* __restrict__ dy, const float* __restrict__ x,
-                                                         const float* __restrict__ r, int64_t rows, int64_t d,
-                                                         float* __restrict__ part) {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// (1024 rows) of dy[n,c] * (x[n,c] * r[n]), from +0 in ascending n. There are
+// only d * chunks chains, so each lane issues the loads of 32 rows before it
+// runs their 32 dependent fmas, keeping many loads in flight per lane.
+constexpr int DW_ROWS = 32;
+__global__ __launch_bounds__(64) void k_rmsnorm_dw_part(const float* __restrict__ dy, const float* __restrict__ x,
+                                                        const float* __restrict__ r, int64_t rows, int64_t d,
+                                                        float* __restrict__ part) {
+    const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
     const int64_t ch = blockIdx.y;
-    if (c >= d) return;
+    const bool live = c < d;
+    const int64_t cc = live ? c : 0;
     const int64_t n0 = ch * KC, n1 = (n0 + KC < rows) ? n0 + KC : rows;
     float acc = 0.0f;
-    for (int64_t n = n0; n < n1; ++n) acc = __builtin_fmaf(dy[n * d + c], x[n * d + c] * r[n], acc);
-    part[ch * d + c] = acc;
+    int64_t n = n0;
+    for (; n + DW_ROWS <= n1; n += DW_ROWS) {
+        float vy[DW_ROWS], vx[DW_ROWS];
+#pragma unroll
+        for (int q = 0; q < DW_ROWS; ++q) {
+            vy[q] = dy[(n + q) * d + cc];
+            vx[q] = x[(n + q) * d + cc] * r[n + q];
+        }
+#pragma unroll
+        for (int q = 0; q < DW_ROWS; ++q) acc = __builtin_fmaf(vy[q], vx[q], acc);
+    }
+    for (; n < n1; ++n) acc = __builtin_fmaf(dy[n * d + cc], x[n * d + cc] * r[n], acc);
+    if (live) part[ch * d + c] = acc;
 }
 
 // Left fold of per-chunk column partials, then dw = t (mode 0) or dw + t (mode 1).
@@ -148,6 +163,43 @@ __global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t 
     for (int64_t j = lane; j < n; j += 64) p[j] = p[j] * rz;
 }
 
+// The same rule with the row held in registers (lane l owns j = l + 64m,
+// m < PER): one read and one write of the row instead of three and two.
+template <int PER>
+__global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int64_t T) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= nbh * T) return;
+    const int64_t i = row % T;
+    float* p = P + row * T;
+    const int64_t n = i + 1;
+    float v[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+        const int64_t j = lane + 64 * m;
+        v[m] = j < n ? p[j] : 0.0f;
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+        if (lane + 64 * m < n) mx = max_keep(mx, v[m]);
+    mx = wave_tree_max(mx);
+    float acc = 0.0f;
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+        if (lane + 64 * m < n) {
+            v[m] = exp_p(v[m] - mx);
+            acc = acc + v[m];
+        }
+    const float Z = wave_tree_sum(acc);
+    const float rz = 1.0f / Z;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+        const int64_t j = lane + 64 * m;
+        if (j < n) p[j] = v[m] * rz;
+    }
+}
+
 // D_i = DOT64 over the head dimension of dO and O, one wavefront per row.
 __global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, const float* __restrict__ O,
                                                 int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
@@ -203,12 +255,12 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(const float* __restrict__ dA
 // loss = log(Z) - (l_y - m); dl = ((exp(l - m) * (1/Z)) - [v == y]) * invN.
 // A target outside [0, V) raises *err and is read as 0 (no out-of-range read).
 __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* __restrict__ tg, int64_t N,
-                                              int64_t V, float invN, float* __restrict__ loss_rows, float* dl,
-                                              int* err) {
+                                              int64_t V, int64_t ld, float invN, float* __restrict__ loss_rows,
+                                              float* dl, int* err) {
     const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (n >= N) return;
-    const float* l = l_in + n * V;
+    const float* l = l_in + n * ld;
     int64_t y = tg[n];
     if (y < 0 || y >= V) {
         if (lane == 0) atomicOr(err, 2);
@@ -223,7 +275,7 @@ __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* 
     const float ly = l[y];
     if (lane == 0) loss_rows[n] = log_p(Z) - (ly - m);
     const float rz = 1.0f / Z;
-    float* o = dl + n * V;
+    float* o = dl + n * ld;
     for (int64_t v = lane; v < V; v += 64) {
         const float p = exp_p(l[v] - m) * rz;
         const float t = (v == y) ? (p - 1.0f) : p;
@@ -407,7 +459,7 @@ int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows
         return ok();
     }
     const int64_t nch = (rows + KC - 1) / KC;
-    k_rmsnorm_dw_part<<<dim3(blocks(d, 256), (unsigned)nch), 256, 0, s>>>(dy, x, r, rows, d, part);
+    k_rmsnorm_dw_part<<<dim3(blocks(d, 64), (unsigned)nch), 64, 0, s>>>(dy, x, r, rows, d, part);
     k_fold_cols<<<blocks(d, 256), 256, 0, s>>>(part, nch, d, dw, mode);
     return ok();
 }
@@ -424,7 +476,9 @@ int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, cons
 int softmax_causal(float* P, int64_t nbh, int64_t T, hipStream_t s) {
     if (nbh < 0 || T < 0) return -1;
     if (nbh * T == 0) return 0;
-    k_softmax<<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
+    if (T <= 512) k_softmax_reg<8><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
+    else if (T <= 2048) k_softmax_reg<32><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
+    else k_softmax<<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
     return ok();
 }
 
@@ -453,12 +507,12 @@ int swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float*
     return ok();
 }
 
-int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, float* loss_rows, float* dl,
-                  int* err, hipStream_t s) {
-    if (N < 0 || V <= 0) return -1;
+int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, int64_t ld, float* loss_rows,
+                  float* dl, int* err, hipStream_t s) {
+    if (N < 0 || V <= 0 || ld < V) return -1;
     if (N == 0) return 0;
     const float invN = 1.0f / (float)N;
-    k_xent<<<blocks(N, 4), 256, 0, s>>>(logits, tg, N, V, invN, loss_rows, dl, err);
+    k_xent<<<blocks(N, 4), 256, 0, s>>>(logits, tg, N, V, ld, invN, loss_rows, dl, err);
     return ok();
 }
 

@@ -28,7 +28,8 @@ extern "C" {
  * C(i,j) = C[i*ldc+j]. mode 0 C = t, 1 C = C + t, 2 C = t * scale. outmask 1
  * writes j <= i only. batch = number of problems, heads divides batch, problem
  * z = zb*heads + zh offsets A by zb*sAb + zh*sAh (same for B, C).
- * Launch choices that never change bits: tile (-1 auto, 0 128x128, 1 256x64),
+ * Launch choices that never change bits: tile (-1 auto, 0 128x128, 1 256x64,
+ * 2 64x64; causal ranges need 2),
  * split (-1 auto, 0 off, 1 per-chunk partials folded by a second kernel; needs
  * ws of ceil(K/1024)*M*N floats), simple (1 = one thread per output). */
 mlb_status mlb_prim_gemm(int64_t M, int64_t N, int64_t K, int64_t kseg, const float* A, int64_t lda, int a_kc,

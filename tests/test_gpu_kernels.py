@@ -332,3 +332,39 @@ def test_adamw(mlb):
     assert_bits("m", host(md), mo)
     assert_bits("v", host(vd), vo)
     assert np.all(host(gd) == 0) and not np.any(np.signbit(host(gd)))
+
+
+def test_segment_split_same_bits(mlb):
+    """The segment-major chunk list folded by the split path equals the in-kernel fold."""
+    rng = np.random.default_rng(15)
+    M, d, F = 200, 160, 1056
+    A, B = make(rng, (M, 2 * F)), make(rng, (2 * F, d))
+    want = orc_contract(A, B, M, d, 2 * F, 2 * F, True, d, False, kseg=F)
+    ws = empty(4 * M * d)
+    for split in (0, 1):
+        C = empty(M * d)
+        mlb.gemm(dev(A), dev(B), C, M, d, 2 * F, 2 * F, True, d, False, d, kseg=F, split=split, ws=ws)
+        assert_bits(f"segments split {split}", host(C).reshape(M, d), want)
+
+
+@pytest.mark.parametrize("layout", ["nt", "nn", "tn"])
+def test_padded_leading_dimension(mlb, layout):
+    """Vector loads over a leading dimension padded past an odd extent (the
+    logits layout): the slack past K (or M) never enters a chain."""
+    rng = np.random.default_rng(16)
+    M, K, N = 130, 1027, 96
+    a_kc, b_kc = layout[0] == "n", layout[1] == "t"
+    ext_a = K if a_kc else M
+    lda = (ext_a + 3) // 4 * 4
+    rows_a = M if a_kc else K
+    Ap = np.full((rows_a, lda), np.nan, np.float32)          # slack holds NaN on purpose
+    Ap[:, :ext_a] = make(rng, (rows_a, ext_a))
+    ext_b = K if b_kc else N
+    ldb = (ext_b + 3) // 4 * 4
+    rows_b = N if b_kc else K
+    Bp = np.full((rows_b, ldb), np.nan, np.float32)
+    Bp[:, :ext_b] = make(rng, (rows_b, ext_b))
+    want = orc_contract(Ap, Bp, M, N, K, lda, a_kc, ldb, b_kc)
+    C = empty(M * N)
+    mlb.gemm(dev(Ap), dev(Bp), C, M, N, K, lda, a_kc, ldb, b_kc, N)
+    assert_bits(f"padded {layout}", host(C).reshape(M, N), want)
