@@ -73,9 +73,9 @@ _SIGS = {
     "mlb_prim_rmsnorm_fwd": (i32, [vp, vp, i64, i64, f32, vp, vp, vp]),
     "mlb_prim_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]),
     "mlb_prim_rope": (i32, [vp, i64, i64, i64, i64, i64, f32, i32, vp]),
-    "mlb_prim_attention_fwd": (i32, [i64, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, vp]),
+    "mlb_prim_attention_fwd": (i32, [i64, i64, i64, i64, vp, vp, vp, i64, vp, vp, i64, i32, vp]),
     "mlb_prim_attention_bwd": (i32, [i64, i64, i64, i64, vp, vp, vp, i64, vp, vp, vp, i64, vp, vp, vp,
-                                     vp, sz, vp]),
+                                     i32, vp, sz, vp]),
     "mlb_prim_swiglu_fwd": (i32, [vp, i64, i64, vp, vp]),
     "mlb_prim_swiglu_bwd": (i32, [vp, vp, i64, i64, vp, vp]),
     "mlb_prim_cross_entropy": (i32, [vp, vp, i64, i64, vp, vp, vp, vp]),
@@ -235,15 +235,22 @@ def rope(x, B, T, H, hd, ld, theta, backward=0, stream=None):
     check(lib().mlb_prim_rope(_ptr(x), B, T, H, hd, ld, float(theta), int(backward), _stream(stream)))
 
 
-def attention_fwd(B, H, T, hd, q, k, v, ld, P, O, ldo, stream=None):
+def attention_fwd(B, H, T, hd, q, k, v, ld, P, O, ldo, tiled=0, stream=None):
     check(lib().mlb_prim_attention_fwd(B, H, T, hd, _ptr(q), _ptr(k), _ptr(v), ld, _ptr(P), _ptr(O), ldo,
-                                       _stream(stream)))
+                                       int(tiled), _stream(stream)))
 
 
-def attention_bwd(B, H, T, hd, q, k, v, ld, P, O, dO, ldo, dq, dk, dv, ws, stream=None):
+def attention_bwd(B, H, T, hd, q, k, v, ld, P, O, dO, ldo, dq, dk, dv, ws, tiled=0, stream=None):
     check(lib().mlb_prim_attention_bwd(B, H, T, hd, _ptr(q), _ptr(k), _ptr(v), ld, _ptr(P), _ptr(O), _ptr(dO), ldo,
-                                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
-                                       _stream(stream)))
+                                       _ptr(dq), _ptr(dk), _ptr(dv), int(tiled), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def tiled_to_dense(P: np.ndarray, T: int) -> np.ndarray:
+    """[..., T*T] in the 32x32 tile layout -> [..., T, T] row-major (host, numpy)."""
+    nt = T // 32
+    x = P.reshape(-1, nt, nt, 32, 32)
+    return np.ascontiguousarray(x.transpose(0, 1, 3, 2, 4)).reshape(-1, T, T)
 
 
 def swiglu_fwd(gu, rows, F, a, stream=None):

@@ -153,6 +153,7 @@ bool cfg_valid(const mlb_config* c, std::string* why) {
 bool cfg_supported(const mlb_config* c, std::string* why) {
     if (c->head_dim % 2) { *why = "rotary pairs need an even head_dim"; return false; }
     if (c->d_model % 32 || c->ffn_hidden % 32) { *why = "d_model and ffn_hidden must be multiples of 32"; return false; }
+    if (c->seq_len % 32) { *why = "seq_len must be a multiple of 32 (32x32 attention tiles)"; return false; }
     if ((uint64_t)c->batch * c->seq_len > (uint64_t)MAX_TOKENS) {
         *why = "more than 8192 tokens per micro-batch";
         return false;
@@ -431,7 +432,7 @@ mlb_status run_tri(mlb_model* M, const char* site, int64_t T, int64_t hd, const 
     const Sizes& s = M->s;
     const int64_t ev = stat_begin(M);
     const int r = mlb::tri_nt(T, hd, s.B * s.H, s.H, A, lda, sAb, hd, B, ldb, sBb, hd, C, T, s.H * T * T, T * T,
-                              scaled, scale, M->stream);
+                              scaled, scale, 1, M->stream);
     stat_end(M, ev, site, "k_tri_nt", 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd,
              0.0);
     if (r != 0) return fail(MLB_E_DEVICE, "%s failed (%d)", site, r);
@@ -467,9 +468,9 @@ mlb_status forward(mlb_model* M) {
         // S = (q . k) * scale, j <= i
         TRI("attn_scores", T, hd, M->qkv[l], 3 * d, T * 3 * d, M->qkv[l] + d, 3 * d, T * 3 * d, M->P[l], 1,
             M->attn_scale);
-        OP("softmax_fwd", f4 * 2 * tri, mlb::softmax_causal(M->P[l], BH, T, st));
+        OP("softmax_fwd", f4 * 2 * tri, mlb::softmax_causal(M->P[l], BH, T, 1, st));
         mlb::GemmDesc pv = head_gemm(s);   // O = P v over j <= i
-        pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.krange = 1;
+        pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.a_blk = true; pv.krange = 1;
         pv.A = M->P[l]; pv.lda = T; pv.a_kc = true; pv.sAb = H * T * T; pv.sAh = T * T;
         pv.B = M->qkv[l] + 2 * d; pv.ldb = 3 * d; pv.b_kc = false; pv.sBb = T * 3 * d; pv.sBh = hd;
         pv.C = M->O[l]; pv.ldc = d; pv.sCb = T * d; pv.sCh = hd;
@@ -522,20 +523,20 @@ mlb_status backward(mlb_model* M) {
         // dP = dO . v, j <= i
         TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f);
         mlb::GemmDesc dv = head_gemm(s);   // dv = P^T dO over i >= j
-        dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.krange = 2;
+        dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.a_blk = true; dv.krange = 2;
         dv.A = M->P[l]; dv.lda = T; dv.a_kc = false; dv.sAb = H * T * T; dv.sAh = T * T;
         dv.B = M->dO; dv.ldb = d; dv.b_kc = false; dv.sBb = T * d; dv.sBh = hd;
         dv.C = M->dqkv + 2 * d; dv.ldc = 3 * d; dv.sCb = T * 3 * d; dv.sCh = hd;
         RUN("attn_dv", dv);
-        OP("softmax_bwd", f4 * 3 * tri, mlb::softmax_bwd(M->P[l], M->dP, M->Dv, BH, T, M->attn_scale, st));
+        OP("softmax_bwd", f4 * 3 * tri, mlb::softmax_bwd(M->P[l], M->dP, M->Dv, BH, T, M->attn_scale, 1, st));
         mlb::GemmDesc dq = head_gemm(s);   // dq = dS k over j <= i
-        dq.M = T; dq.N = hd; dq.K = T; dq.kseg = T; dq.krange = 1;
+        dq.M = T; dq.N = hd; dq.K = T; dq.kseg = T; dq.a_blk = true; dq.krange = 1;
         dq.A = M->dP; dq.lda = T; dq.a_kc = true; dq.sAb = H * T * T; dq.sAh = T * T;
         dq.B = M->qkv[l] + d; dq.ldb = 3 * d; dq.b_kc = false; dq.sBb = T * 3 * d; dq.sBh = hd;
         dq.C = M->dqkv; dq.ldc = 3 * d; dq.sCb = T * 3 * d; dq.sCh = hd;
         RUN("attn_dq", dq);
         mlb::GemmDesc dk = head_gemm(s);   // dk = dS^T q over i >= j
-        dk.M = T; dk.N = hd; dk.K = T; dk.kseg = T; dk.krange = 2;
+        dk.M = T; dk.N = hd; dk.K = T; dk.kseg = T; dk.a_blk = true; dk.krange = 2;
         dk.A = M->dP; dk.lda = T; dk.a_kc = false; dk.sAb = H * T * T; dk.sAh = T * T;
         dk.B = M->qkv[l]; dk.ldb = 3 * d; dk.b_kc = false; dk.sBb = T * 3 * d; dk.sBh = hd;
         dk.C = M->dqkv + d; dk.ldc = 3 * d; dk.sCb = T * 3 * d; dk.sCh = hd;
@@ -827,11 +828,20 @@ mlb_status mlb_read_stage(const mlb_model* M, int stage, int layer, void* dst, s
     if (bytes < (size_t)n * 4) return fail(MLB_E_IO, "buffer too small");
     HIPCHK(hipSetDevice(M->device));
     HIPCHK(hipStreamSynchronize(M->stream));
-    if (stage == 12)
+    if (stage == 12) {
         HIPCHK(hipMemcpy2D(dst, (size_t)s.V * 4, src, (size_t)s.ldV * 4, (size_t)s.V * 4, (size_t)s.N,
                            hipMemcpyDeviceToHost));
-    else
+    } else if (stage == 4) {   // tiled on the device, dense [B*H, T, T] for the caller
+        std::vector<float> tmp((size_t)n);
+        HIPCHK(hipMemcpy(tmp.data(), src, (size_t)n * 4, hipMemcpyDeviceToHost));
+        float* o = static_cast<float*>(dst);
+        for (int64_t z = 0; z < s.B * s.H; ++z)
+            for (int64_t i = 0; i < s.T; ++i)
+                for (int64_t j = 0; j < s.T; ++j)
+                    o[(z * s.T + i) * s.T + j] = tmp[(size_t)(z * s.T * s.T + mlb::blk_index(s.T, i, j))];
+    } else {
         HIPCHK(hipMemcpy(dst, src, (size_t)n * 4, hipMemcpyDeviceToHost));
+    }
     return MLB_OK;
 }
 
@@ -961,13 +971,15 @@ mlb_status mlb_prim_rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, 
 }
 
 mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, const float* k,
-                                  const float* v, int64_t ld, float* P, float* O, int64_t ldo, void* stream) {
+                                  const float* v, int64_t ld, float* P, float* O, int64_t ldo, int p_tiled, void* stream) {
     if (!q || !k || !v || !P || !O || B <= 0 || H <= 0 || T <= 0 || hd <= 0) return fail(MLB_E_INVALID_ARG, "attention");
+    if (p_tiled && (T % 32 || hd > 64)) return fail(MLB_E_UNSUPPORTED, "tiled P needs T % 32 == 0 and hd <= 64");
     hipStream_t st = static_cast<hipStream_t>(stream);
     mlb::GemmPlan plan;
     const float scale = (float)(1.0 / std::sqrt((double)hd));
     if (hd <= 64) {
-        if (mlb::tri_nt(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T, H * T * T, T * T, 1, scale, st))
+        if (mlb::tri_nt(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T, H * T * T, T * T, 1, scale,
+                        p_tiled, st))
             return fail(MLB_E_DEVICE, "scores");
     } else {
         mlb::GemmDesc sg;
@@ -979,10 +991,10 @@ mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
         sg.outmask = 1; sg.mode = 2; sg.scale = scale;
         if (mlb::gemm(sg, plan, st)) return fail(MLB_E_DEVICE, "scores");
     }
-    if (mlb::softmax_causal(P, B * H, T, st)) return fail(MLB_E_DEVICE, "softmax");
+    if (mlb::softmax_causal(P, B * H, T, p_tiled, st)) return fail(MLB_E_DEVICE, "softmax");
     mlb::GemmDesc pv;
     pv.batch = B * H; pv.H = H;
-    pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.krange = 1;
+    pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.krange = 1; pv.a_blk = p_tiled != 0;
     pv.A = P; pv.lda = T; pv.a_kc = true; pv.sAb = H * T * T; pv.sAh = T * T;
     pv.B = v; pv.ldb = ld; pv.b_kc = false; pv.sBb = T * ld; pv.sBh = hd;
     pv.C = O; pv.ldc = ldo; pv.sCb = T * ldo; pv.sCh = hd;
@@ -992,10 +1004,11 @@ mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
 
 mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, const float* k,
                                   const float* v, int64_t ld, const float* P, const float* O, const float* dO,
-                                  int64_t ldo, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                  int64_t ldo, float* dq, float* dk, float* dv, int p_tiled, void* ws, size_t ws_bytes,
                                   void* stream) {
     if (!q || !k || !v || !P || !O || !dO || !dq || !dk || !dv || B <= 0 || H <= 0 || T <= 0 || hd <= 0)
         return fail(MLB_E_INVALID_ARG, "attention_bwd");
+    if (p_tiled && (T % 32 || hd > 64)) return fail(MLB_E_UNSUPPORTED, "tiled P needs T % 32 == 0 and hd <= 64");
     const size_t need = (size_t)(B * H * T * T + B * H * T) * 4;
     if (!ws || ws_bytes < need) return fail(MLB_E_ARENA_TOO_SMALL, "attention_bwd needs %zu bytes", need);
     float* dP = static_cast<float*>(ws);
@@ -1005,7 +1018,8 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     const float scale = (float)(1.0 / std::sqrt((double)hd));
     if (mlb::attn_rowdot(dO, O, B, H, T, hd, ldo, D, st)) return fail(MLB_E_DEVICE, "rowdot");
     if (hd <= 64) {
-        if (mlb::tri_nt(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T, H * T * T, T * T, 0, 1.0f, st))
+        if (mlb::tri_nt(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T, H * T * T, T * T, 0, 1.0f,
+                        p_tiled, st))
             return fail(MLB_E_DEVICE, "dP");
     } else {
         mlb::GemmDesc g;
@@ -1018,22 +1032,22 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     }
     mlb::GemmDesc gv;
     gv.batch = B * H; gv.H = H;
-    gv.M = T; gv.N = hd; gv.K = T; gv.kseg = T; gv.krange = 2;
+    gv.M = T; gv.N = hd; gv.K = T; gv.kseg = T; gv.krange = 2; gv.a_blk = p_tiled != 0;
     gv.A = P; gv.lda = T; gv.a_kc = false; gv.sAb = H * T * T; gv.sAh = T * T;
     gv.B = dO; gv.ldb = ldo; gv.b_kc = false; gv.sBb = T * ldo; gv.sBh = hd;
     gv.C = dv; gv.ldc = ld; gv.sCb = T * ld; gv.sCh = hd;
     if (mlb::gemm(gv, plan, st)) return fail(MLB_E_DEVICE, "dv");
-    if (mlb::softmax_bwd(P, dP, D, B * H, T, scale, st)) return fail(MLB_E_DEVICE, "softmax_bwd");
+    if (mlb::softmax_bwd(P, dP, D, B * H, T, scale, p_tiled, st)) return fail(MLB_E_DEVICE, "softmax_bwd");
     mlb::GemmDesc gq;
     gq.batch = B * H; gq.H = H;
-    gq.M = T; gq.N = hd; gq.K = T; gq.kseg = T; gq.krange = 1;
+    gq.M = T; gq.N = hd; gq.K = T; gq.kseg = T; gq.krange = 1; gq.a_blk = p_tiled != 0;
     gq.A = dP; gq.lda = T; gq.a_kc = true; gq.sAb = H * T * T; gq.sAh = T * T;
     gq.B = k; gq.ldb = ld; gq.b_kc = false; gq.sBb = T * ld; gq.sBh = hd;
     gq.C = dq; gq.ldc = ld; gq.sCb = T * ld; gq.sCh = hd;
     if (mlb::gemm(gq, plan, st)) return fail(MLB_E_DEVICE, "dq");
     mlb::GemmDesc gk;
     gk.batch = B * H; gk.H = H;
-    gk.M = T; gk.N = hd; gk.K = T; gk.kseg = T; gk.krange = 2;
+    gk.M = T; gk.N = hd; gk.K = T; gk.kseg = T; gk.krange = 2; gk.a_blk = p_tiled != 0;
     gk.A = dP; gk.lda = T; gk.a_kc = false; gk.sAb = H * T * T; gk.sAh = T * T;
     gk.B = q; gk.ldb = ld; gk.b_kc = false; gk.sBb = T * ld; gk.sBh = hd;
     gk.C = dk; gk.ldc = ld; gk.sCb = T * ld; gk.sCh = hd;

@@ -29,6 +29,8 @@ struct TriArgs {
     int scaled;
     float scale;
     int64_t nt;   // tiles per edge
+    int vec;      // float4 loads: K % 4 == 0, 16-byte aligned rows and offsets
+    int blk;      // C in the tiled 32x32 layout
 };
 
 __global__ __launch_bounds__(256) void k_tri_nt(TriArgs a) {
@@ -49,17 +51,42 @@ __global__ __launch_bounds__(256) void k_tri_nt(TriArgs a) {
     const float* B = a.B + zb * a.sBb + zh * a.sBh;
     float* C = a.C + zb * a.sCb + zh * a.sCh;
 
-    for (int q = tid; q < TT * KMAX; q += 256) {
-        const int r = q / KMAX, k = q % KMAX;
-        const int64_t gi = i0 + r, gj = j0 + r;
-        float av, bv;
-        if (k >= a.K) { av = -0.0f; bv = 0.0f; }
-        else {
-            av = gi < a.T ? A[gi * a.lda + k] : 0.0f;
-            bv = gj < a.T ? B[gj * a.ldb + k] : 0.0f;
+    if (a.vec) {
+        // all 16 float4 loads of this thread in flight before any LDS store
+        float4 va[8], vb[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int q = tid + 256 * s, r = q / (KMAX / 4), k = (q % (KMAX / 4)) * 4;
+            const int64_t gi = i0 + r, gj = j0 + r;
+            va[s] = (gi < a.T && k < a.K) ? *reinterpret_cast<const float4*>(A + gi * a.lda + k)
+                                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            vb[s] = (gj < a.T && k < a.K) ? *reinterpret_cast<const float4*>(B + gj * a.ldb + k)
+                                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
-        As[r * LD + k] = av;
-        Bs[r * LD + k] = bv;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int q = tid + 256 * s, r = q / (KMAX / 4), k = (q % (KMAX / 4)) * 4;
+            const float av[4] = {va[s].x, va[s].y, va[s].z, va[s].w};
+            const float bv[4] = {vb[s].x, vb[s].y, vb[s].z, vb[s].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                As[r * LD + k + e] = (k + e >= a.K) ? -0.0f : av[e];
+                Bs[r * LD + k + e] = (k + e >= a.K) ? 0.0f : bv[e];
+            }
+        }
+    } else {
+        for (int q = tid; q < TT * KMAX; q += 256) {
+            const int r = q / KMAX, k = q % KMAX;
+            const int64_t gi = i0 + r, gj = j0 + r;
+            float av, bv;
+            if (k >= a.K) { av = -0.0f; bv = 0.0f; }
+            else {
+                av = gi < a.T ? A[gi * a.lda + k] : 0.0f;
+                bv = gj < a.T ? B[gj * a.ldb + k] : 0.0f;
+            }
+            As[r * LD + k] = av;
+            Bs[r * LD + k] = bv;
+        }
     }
     __syncthreads();
 
@@ -82,7 +109,11 @@ __global__ __launch_bounds__(256) void k_tri_nt(TriArgs a) {
         for (int e = 0; e < 16; ++e) {
             const int64_t gi = i0 + wm * 64 + rbase + 8 * (e >> 2) + 4 * lk + (e & 3);
             const int64_t gj = j0 + wn * 64 + cbase + li;
-            if (gi < a.T && gj <= gi) C[gi * a.ldc + gj] = a.scaled ? v[e] * a.scale : v[e];
+            if (gi < a.T && gj <= gi) {
+                const int64_t o = a.blk ? ((((gi >> 5) * (a.ldc >> 5) + (gj >> 5)) << 10) + ((gi & 31) << 5) + (gj & 31))
+                                        : gi * a.ldc + gj;
+                C[o] = a.scaled ? v[e] * a.scale : v[e];
+            }
         }
     };
     store(c00, 0, 0);
@@ -95,10 +126,14 @@ __global__ __launch_bounds__(256) void k_tri_nt(TriArgs a) {
 
 int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
            const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
-           int scaled, float scale, hipStream_t s) {
+           int scaled, float scale, int blk, hipStream_t s) {
     if (T < 0 || K < 1 || K > KMAX || batch < 1 || H < 1 || batch % H) return -1;
+    if (blk && (ldc % 32 != 0 || ldc < T)) return -1;
     if (T == 0) return 0;
-    TriArgs a{T, K, H, A, lda, sAb, sAh, B, ldb, sBb, sBh, C, ldc, sCb, sCh, scaled, scale, (T + TT - 1) / TT};
+    const bool vec = K % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && sAb % 4 == 0 && sAh % 4 == 0 && sBb % 4 == 0 &&
+                     sBh % 4 == 0 && ((uintptr_t)A & 15u) == 0 && ((uintptr_t)B & 15u) == 0;
+    TriArgs a{T, K, H, A, lda, sAb, sAh, B, ldb, sBb, sBh, C, ldc, sCb, sCh, scaled, scale, (T + TT - 1) / TT,
+              vec ? 1 : 0, blk ? 1 : 0};
     const int64_t ntri = a.nt * (a.nt + 1) / 2;
     k_tri_nt<<<dim3((unsigned)ntri, 1, (unsigned)batch), 256, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -3;

@@ -34,7 +34,7 @@ namespace mlb {
 namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-constexpr int KT = 32;
+constexpr int KTMIN = 32;   // K tiles are 32 or 64 wide; both divide the 1024 chunk
 constexpr int64_t KC = 1024;
 
 struct KArgs {
@@ -50,6 +50,13 @@ struct KArgs {
     int64_t tiles_m, tiles_n, ntiles;
 };
 
+// Offset of element (r, c) of a matrix stored as 32x32 tiles, each 4 KiB
+// contiguous and row-major inside, tiles row-major; ld is the logical row length
+// (a multiple of 32).
+__device__ __forceinline__ int64_t blk_off(int64_t ld, int64_t r, int64_t c) {
+    return (((r >> 5) * (ld >> 5) + (c >> 5)) << 10) + ((r & 31) << 5) + (c & 31);
+}
+
 __device__ __forceinline__ void epilogue_store(const KArgs& a, float* C, int64_t gi, int64_t gj, float v) {
     float* p = C + gi * a.ldc + gj;
     if (a.mode == 0) *p = v;
@@ -58,7 +65,7 @@ __device__ __forceinline__ void epilogue_store(const KArgs& a, float* C, int64_t
     else *p = a.R[gi * a.ldc + gj] + v;
 }
 
-template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, bool VEC, bool MC>
+template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, bool VEC, bool MC, int KT, bool ABLK = false>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     // Each wave owns RB 32-row blocks x 64 columns (two 32x32 MFMA blocks per
     // row block). MC: the contraction may span several 1024-chunks, so a
@@ -133,13 +140,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
                 // the leading dimension covers the vector past the last element;
                 // positions past K read as -0, rows past M as 0
                 if (gk < a.K && gi < a.M) {
-                    const float4 v = AKC ? *reinterpret_cast<const float4*>(A + gi * a.lda + gk)
+                    const float4 v = ABLK ? *reinterpret_cast<const float4*>(A + blk_off(a.lda, AKC ? gi : gk, AKC ? gk : gi))
+                                   : AKC ? *reinterpret_cast<const float4*>(A + gi * a.lda + gk)
                                          : *reinterpret_cast<const float4*>(A + gk * a.lda + gi);
+                    // positions past K inside the vector are masked at the LDS store,
+                    // so that no select waits on the load here
                     ra[s * 4 + 0] = v.x; ra[s * 4 + 1] = v.y; ra[s * 4 + 2] = v.z; ra[s * 4 + 3] = v.w;
-                    if (AKC) {
-#pragma unroll
-                        for (int e = 1; e < 4; ++e) if (gk + e >= a.K) ra[s * 4 + e] = -0.0f;
-                    }
                 } else {
                     const float f = (gk >= a.K) ? -0.0f : 0.0f;
                     ra[s * 4 + 0] = f; ra[s * 4 + 1] = f; ra[s * 4 + 2] = f; ra[s * 4 + 3] = f;
@@ -147,7 +153,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
             } else {
                 if (gk >= a.K) ra[s] = -0.0f;
                 else if (gi >= a.M) ra[s] = 0.0f;
-                else ra[s] = AKC ? A[gi * a.lda + gk] : A[gk * a.lda + gi];
+                else ra[s] = ABLK ? A[blk_off(a.lda, AKC ? gi : gk, AKC ? gk : gi)]
+                           : AKC ? A[gi * a.lda + gk] : A[gk * a.lda + gi];
             }
         }
 #pragma unroll
@@ -161,10 +168,6 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
                     const float4 v = BKC ? *reinterpret_cast<const float4*>(B + gj * a.ldb + gk)
                                          : *reinterpret_cast<const float4*>(B + gk * a.ldb + gj);
                     rb[s * 4 + 0] = v.x; rb[s * 4 + 1] = v.y; rb[s * 4 + 2] = v.z; rb[s * 4 + 3] = v.w;
-                    if (BKC) {
-#pragma unroll
-                        for (int e = 1; e < 4; ++e) if (gk + e >= a.K) rb[s * 4 + e] = 0.0f;
-                    }
                 } else {
                     rb[s * 4 + 0] = 0.0f; rb[s * 4 + 1] = 0.0f; rb[s * 4 + 2] = 0.0f; rb[s * 4 + 3] = 0.0f;
                 }
@@ -174,14 +177,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
             }
         }
     };
-    auto store_lds = [&]() {
+    auto store_lds = [&](int64_t kt) {
+        const int64_t k0 = kt * KT;
 #pragma unroll
         for (int s = 0; s < EA; ++s) {
             const int q = tid + s * NTHR;
             if (AKC) {
                 const int i = q / (KT / W), k = (q % (KT / W)) * W;
 #pragma unroll
-                for (int e = 0; e < W; ++e) As[i * ALD + k + e] = ra[s * W + e];
+                for (int e = 0; e < W; ++e)
+                    As[i * ALD + k + e] = (VEC && e > 0 && k0 + k + e >= a.K) ? -0.0f : ra[s * W + e];
             } else {
                 const int k = q / (MT / W), i = (q % (MT / W)) * W;
 #pragma unroll
@@ -194,7 +199,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
             if (BKC) {
                 const int j = q / (KT / W), k = (q % (KT / W)) * W;
 #pragma unroll
-                for (int e = 0; e < W; ++e) Bs[j * BLD + k + e] = rb[s * W + e];
+                for (int e = 0; e < W; ++e)
+                    Bs[j * BLD + k + e] = (VEC && e > 0 && k0 + k + e >= a.K) ? 0.0f : rb[s * W + e];
             } else {
                 const int k = q / (NT / W), j = (q % (NT / W)) * W;
 #pragma unroll
@@ -218,10 +224,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     };
     const int j0l = wn * 64 + li, j1l = j0l + 32;
     // one 32-row block against the wave's two 32-column blocks, all 16 k-pairs
-    auto full_block = [&](v16f& c0, v16f& c1, int rloc) {
+    auto full_block = [&](v16f& c0, v16f& c1, int rloc, int ko) {
 #pragma unroll 4
-        for (int p = 0; p < KT / 2; ++p) {
-            const int kk = 2 * p + lk;
+        for (int p = 0; p < 16; ++p) {
+            const int kk = ko + 2 * p + lk;
             const float av = a_lds(rloc + li, kk);
             const float b0 = b_lds(kk, j0l), b1 = b_lds(kk, j1l);
             c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, c0, 0, 0, 0);
@@ -235,18 +241,18 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     // boundary falls between them (il == ka, resp. il == kb) takes the single
     // term with one fma; every other row keeps its value. Positions past K are
     // padded (-0 * +0) and change nothing.
-    auto diag_block = [&](v16f& c0, v16f& c1, int rloc) {
+    auto diag_block = [&](v16f& c0, v16f& c1, int rloc, int ko) {
 #pragma unroll 1
-        for (int p = 0; p < KT / 2; ++p) {
-            const int kk = 2 * p + lk;
+        for (int p = 0; p < 16; ++p) {
+            const int kk = ko + 2 * p + lk;
             const float av = a_lds(rloc + li, kk);
             const float b0 = b_lds(kk, j0l), b1 = b_lds(kk, j1l);
             const v16f n0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b0, c0, 0, 0, 0);
             const v16f n1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b1, c1, 0, 0, 0);
-            const int ka = 2 * p, kb = 2 * p + 1;
+            const int ka = 2 * p, kb = 2 * p + 1;              // relative to the block's first row
             const int ks = (KR == 1) ? ka : kb;               // the single term's k, also its row
-            const float as = a_lds(rloc + ks, ks);
-            const float bs0 = b_lds(ks, j0l), bs1 = b_lds(ks, j1l);
+            const float as = a_lds(rloc + ks, ko + ks);
+            const float bs0 = b_lds(ko + ks, j0l), bs1 = b_lds(ko + ks, j1l);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int il = 8 * (e >> 2) + 4 * lk + (e & 3);
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     for (int64_t kt = kt0; kt < kt1; ++kt) {
         const int64_t k0 = kt * KT;
         __syncthreads();
-        store_lds();
+        store_lds(kt);
         __syncthreads();
         if (kt + 1 < kt1) load_global(kt + 1);
         if (MC) {
@@ -278,36 +284,41 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
                 prev_chunk = chunk;
             }
         }
-        // per row block: 0 skip, 1 full tile, 2 diagonal tile
-        int st0 = 1, st1 = 1;
-        if (KR == 1) {
-            st0 = (k0 < bi00) ? 1 : (k0 == bi00 ? 2 : 0);
-            st1 = (k0 < bi01) ? 1 : (k0 == bi01 ? 2 : 0);
-        } else if (KR == 2) {
-            st0 = (k0 > bi00) ? 1 : (k0 == bi00 ? 2 : 0);
-            st1 = (k0 > bi01) ? 1 : (k0 == bi01 ? 2 : 0);
-        }
-        dirty0 = dirty0 || st0 != 0;
-        dirty1 = dirty1 || st1 != 0;
-        if (RB == 2 && st0 == 1 && st1 == 1) {
-#pragma unroll 4
-            for (int p = 0; p < KT / 2; ++p) {
-                const int kk = 2 * p + lk;
-                const float a0 = a_lds(r0 + li, kk);
-                const float a1 = a_lds(r1 + li, kk);
-                const float b0 = b_lds(kk, j0l);
-                const float b1 = b_lds(kk, j1l);
-                acc00 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc00, 0, 0, 0);
-                acc01 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc01, 0, 0, 0);
-                acc10 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc10, 0, 0, 0);
-                acc11 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc11, 0, 0, 0);
+        // 32-wide sub-tiles of the K tile; per row block: 0 skip, 1 full, 2 diagonal
+#pragma unroll
+        for (int h = 0; h < KT / 32; ++h) {
+            const int64_t k0h = k0 + 32 * h;
+            const int ko = 32 * h;
+            int st0 = 1, st1 = 1;
+            if (KR == 1) {
+                st0 = (k0h < bi00) ? 1 : (k0h == bi00 ? 2 : 0);
+                st1 = (k0h < bi01) ? 1 : (k0h == bi01 ? 2 : 0);
+            } else if (KR == 2) {
+                st0 = (k0h > bi00) ? 1 : (k0h == bi00 ? 2 : 0);
+                st1 = (k0h > bi01) ? 1 : (k0h == bi01 ? 2 : 0);
             }
-        } else {
-            if (st0 == 1) full_block(acc00, acc01, r0);
-            else if (KR != 0 && st0 == 2) diag_block(acc00, acc01, r0);
-            if (RB == 2) {
-                if (st1 == 1) full_block(acc10, acc11, r1);
-                else if (KR != 0 && st1 == 2) diag_block(acc10, acc11, r1);
+            dirty0 = dirty0 || st0 != 0;
+            dirty1 = dirty1 || st1 != 0;
+            if (RB == 2 && st0 == 1 && st1 == 1) {
+#pragma unroll 4
+                for (int p = 0; p < 16; ++p) {
+                    const int kk = ko + 2 * p + lk;
+                    const float a0 = a_lds(r0 + li, kk);
+                    const float a1 = a_lds(r1 + li, kk);
+                    const float b0 = b_lds(kk, j0l);
+                    const float b1 = b_lds(kk, j1l);
+                    acc00 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc00, 0, 0, 0);
+                    acc01 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc01, 0, 0, 0);
+                    acc10 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc10, 0, 0, 0);
+                    acc11 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc11, 0, 0, 0);
+                }
+            } else {
+                if (st0 == 1) full_block(acc00, acc01, r0, ko);
+                else if (KR != 0 && st0 == 2) diag_block(acc00, acc01, r0, ko);
+                if (RB == 2) {
+                    if (st1 == 1) full_block(acc10, acc11, r1, ko);
+                    else if (KR != 0 && st1 == 2) diag_block(acc10, acc11, r1, ko);
+                }
             }
         }
     }
@@ -393,16 +404,17 @@ struct Cfg { int wm, wn; };
 
 thread_local char g_launched[96];
 
-template <bool AKC, bool BKC, int WM, int WN, int RB, int KR>
+template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, int KT = 32, bool ABLK = false>
 void launch_t(const KArgs& a, bool vec, bool mc, dim3 grid, hipStream_t s) {
-    std::snprintf(g_launched, sizeof g_launched, "k_gemm<%s, %s, %d, %d, %d, %d, %s, %s>", AKC ? "true" : "false",
-                  BKC ? "true" : "false", WM, WN, RB, KR, vec ? "true" : "false", (KR != 0 || mc) ? "true" : "false");
+    std::snprintf(g_launched, sizeof g_launched, "k_gemm<%s, %s, %d, %d, %d, %d, %s, %s, %d, %s>",
+                  AKC ? "true" : "false", BKC ? "true" : "false", WM, WN, RB, KR, vec ? "true" : "false",
+                  (KR != 0 || mc) ? "true" : "false", KT, ABLK ? "true" : "false");
     if (KR != 0 || mc) {
-        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, true><<<grid, 64 * WM * WN, 0, s>>>(a);
-        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, true><<<grid, 64 * WM * WN, 0, s>>>(a);
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
+        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
     } else {
-        if (vec) k_gemm<AKC, BKC, WM, WN, RB, 0, true, false><<<grid, 64 * WM * WN, 0, s>>>(a);
-        else k_gemm<AKC, BKC, WM, WN, RB, 0, false, false><<<grid, 64 * WM * WN, 0, s>>>(a);
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, 0, true, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
+        else k_gemm<AKC, BKC, WM, WN, RB, 0, false, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
     }
 }
 
@@ -432,8 +444,18 @@ bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_
             case 2: launch_t<false, true, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
         }
     }
-    if (d.krange == 1 && key == 1 && cfg == 2) { launch_t<true, false, 4, 1, 1, 1>(a, vec, mc, grid, s); return true; }
-    if (d.krange == 2 && key == 0 && cfg == 2) { launch_t<false, false, 4, 1, 1, 2>(a, vec, mc, grid, s); return true; }
+    // causal ranges; a tiled A (32x32 blocks, the attention probability layout)
+    // is read as whole contiguous 4 KiB tiles
+    if (d.krange == 1 && key == 1 && cfg == 2) {
+        if (d.a_blk) launch_t<true, false, 4, 1, 1, 1, 32, true>(a, vec, mc, grid, s);
+        else launch_t<true, false, 4, 1, 1, 1, 32>(a, vec, mc, grid, s);
+        return true;
+    }
+    if (d.krange == 2 && key == 0 && cfg == 2) {
+        if (d.a_blk) launch_t<false, false, 4, 1, 1, 2, 32, true>(a, vec, mc, grid, s);
+        else launch_t<false, false, 4, 1, 1, 2, 32>(a, vec, mc, grid, s);
+        return true;
+    }
     return false;
 }
 
@@ -446,8 +468,9 @@ static bool desc_ok(const GemmDesc& d) {
     if (d.krange < 0 || d.krange > 2 || d.mode < 0 || d.mode > 3) return false;
     if (d.mode == 3 && (!d.R || d.batch != 1)) return false;
     if (d.K > 0 && (d.kseg <= 0 || d.K % d.kseg != 0)) return false;
-    if (d.K > 0 && d.K / d.kseg > 1 && (d.kseg % KT != 0 || d.krange != 0)) return false;
+    if (d.K > 0 && d.K / d.kseg > 1 && (d.kseg % KTMIN != 0 || d.krange != 0)) return false;
     if (!d.A || !d.B || !d.C) return false;
+    if (d.a_blk && (d.lda % 32 != 0 || d.krange == 0 || (d.a_kc ? d.M : d.K) > d.lda)) return false;
     return true;
 }
 

@@ -21,6 +21,9 @@ namespace mlb {
 struct GemmDesc {
     int64_t M = 0, N = 0, K = 0, kseg = 0;
     const float* A = nullptr; int64_t lda = 0; bool a_kc = true;
+    // A stored as 32x32 tiles (blk layout below) with logical row length lda;
+    // a_kc then means A(i,k) = X(i,k), else A(i,k) = X(k,i). Causal ranges only.
+    bool a_blk = false;
     const float* B = nullptr; int64_t ldb = 0; bool b_kc = true;
     float* C = nullptr; int64_t ldc = 0;
     const float* R = nullptr;
@@ -29,6 +32,14 @@ struct GemmDesc {
     int krange = 0, outmask = 0, mode = 0;
     float scale = 1.0f;
 };
+
+// Tiled square layout of the attention matrices P and dS: element (r, c) of a
+// matrix with logical row length ld (a multiple of 32) sits at
+// ((r/32)*(ld/32) + c/32)*1024 + (r%32)*32 + c%32, so every 32x32 tile is one
+// contiguous 4 KiB run.
+inline int64_t blk_index(int64_t ld, int64_t r, int64_t c) {
+    return ((r / 32) * (ld / 32) + c / 32) * 1024 + (r % 32) * 32 + (c % 32);
+}
 
 // Host-side launch options. They never change a result bit: the split and
 // tile choices only change which workgroup computes which chunk.
@@ -51,9 +62,10 @@ const char* gemm_last_kernel();
 // Lower triangle of a batched contraction over a short K (<= 64, one chunk):
 // C(i,j) = t(i,j) (times scale when scaled) for j <= i < T, with
 // t(i,j) = fma chain over k of A[i*lda + k] * B[j*ldb + k] (mlb_attn.hip).
+// blk: C is stored in the tiled layout (ldc = T, a multiple of 32).
 int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
            const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
-           int scaled, float scale, hipStream_t s);
+           int scaled, float scale, int blk, hipStream_t s);
 
 // Row and elementwise kernels (mlb_ops.hip). All return 0 or a negative value
 // on invalid sizes; they launch on stream s and never synchronise.
@@ -70,13 +82,14 @@ int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows
                    float* dw, int mode, hipStream_t s);
 int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, const float* cosv,
          const float* sinv, int backward, hipStream_t s);
-// In-place causal softmax of rows i of [nbh, T, T] over j <= i.
-int softmax_causal(float* P, int64_t nbh, int64_t T, hipStream_t s);
+// In-place causal softmax of rows i of [nbh, T, T] over j <= i (blk: tiled
+// layout, T a multiple of 32).
+int softmax_causal(float* P, int64_t nbh, int64_t T, int blk, hipStream_t s);
 // D[z*T + i] = DOT64 over hd of dO and O rows (head layout as q).
 int attn_rowdot(const float* dO, const float* O, int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
                 float* D, hipStream_t s);
 // dS = (P * (dP - D_i)) * scale in place over dP, j <= i.
-int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t T, float scale,
+int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t T, float scale, int blk,
                 hipStream_t s);
 int swiglu_fwd(const float* gu, int64_t rows, int64_t F, float* a, hipStream_t s);
 int swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float* dgu, hipStream_t s);

@@ -16,6 +16,12 @@ constexpr int64_t KC = 1024;
 
 inline unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
+// Position of element j of row i in a [T, T] matrix, row-major or tiled
+// (32x32 tiles of 4 KiB, see blk_index).
+__device__ __forceinline__ int64_t pos(int blk, int64_t T, int64_t i, int64_t j) {
+    return blk ? ((((i >> 5) * (T >> 5) + (j >> 5)) << 10) + ((i & 31) << 5) + (j & 31)) : i * T + j;
+}
+
 // Embedding lookup: an exact copy of table row ids[n]. An id outside [0, V)
 // writes zeros and raises *err (no out-of-range read).
 __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ ids, const float* __restrict__ tab,
@@ -142,42 +148,42 @@ __global__ __launch_bounds__(256) void k_rope(float* x, int64_t B, int64_t T, in
 
 // Causal softmax in place, one wavefront per row i over j <= i:
 // m = MAX64, e = exp(S - m), Z = SUM64(e), P = e * (1 / Z).
-__global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t T) {
+__global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t T, int blk) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= nbh * T) return;
     const int64_t i = row % T;
-    float* p = P + row * T;
+    float* p = P + (row / T) * T * T;
     const int64_t n = i + 1;
     float m = -__builtin_inff();
-    for (int64_t j = lane; j < n; j += 64) m = max_keep(m, p[j]);
+    for (int64_t j = lane; j < n; j += 64) m = max_keep(m, p[pos(blk, T, i, j)]);
     m = wave_tree_max(m);
     float acc = 0.0f;
     for (int64_t j = lane; j < n; j += 64) {
-        const float e = exp_p(p[j] - m);
-        p[j] = e;
+        const float e = exp_p(p[pos(blk, T, i, j)] - m);
+        p[pos(blk, T, i, j)] = e;
         acc = acc + e;
     }
     const float Z = wave_tree_sum(acc);
     const float rz = 1.0f / Z;
-    for (int64_t j = lane; j < n; j += 64) p[j] = p[j] * rz;
+    for (int64_t j = lane; j < n; j += 64) p[pos(blk, T, i, j)] = p[pos(blk, T, i, j)] * rz;
 }
 
 // The same rule with the row held in registers (lane l owns j = l + 64m,
 // m < PER): one read and one write of the row instead of three and two.
 template <int PER>
-__global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int64_t T) {
+__global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int64_t T, int blk) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= nbh * T) return;
     const int64_t i = row % T;
-    float* p = P + row * T;
+    float* p = P + (row / T) * T * T;
     const int64_t n = i + 1;
     float v[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         const int64_t j = lane + 64 * m;
-        v[m] = j < n ? p[j] : 0.0f;
+        v[m] = j < n ? p[pos(blk, T, i, j)] : 0.0f;
     }
     float mx = -__builtin_inff();
 #pragma unroll
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int6
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         const int64_t j = lane + 64 * m;
-        if (j < n) p[j] = v[m] * rz;
+        if (j < n) p[pos(blk, T, i, j)] = v[m] * rz;
     }
 }
 
@@ -217,12 +223,14 @@ __global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, co
 
 // dS = (P * (dP - D_i)) * scale over j <= i, written over dP.
 __global__ __launch_bounds__(256) void k_softmax_bwd(const float* __restrict__ P, float* dP,
-                                                     const float* __restrict__ D, int64_t T, float scale) {
+                                                     const float* __restrict__ D, int64_t T, float scale, int blk) {
     const int64_t i = blockIdx.x, z = blockIdx.y;
-    const int64_t base = (z * T + i) * T;
+    const int64_t base = z * T * T;
     const float Di = D[z * T + i];
-    for (int64_t j = threadIdx.x; j <= i; j += blockDim.x)
-        dP[base + j] = (P[base + j] * (dP[base + j] - Di)) * scale;
+    for (int64_t j = threadIdx.x; j <= i; j += blockDim.x) {
+        const int64_t o = base + pos(blk, T, i, j);
+        dP[o] = (P[o] * (dP[o] - Di)) * scale;
+    }
 }
 
 // SwiGLU: sig = 1 / (1 + exp(-g)); a = (g * sig) * u.
@@ -473,12 +481,12 @@ int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, cons
     return ok();
 }
 
-int softmax_causal(float* P, int64_t nbh, int64_t T, hipStream_t s) {
-    if (nbh < 0 || T < 0) return -1;
+int softmax_causal(float* P, int64_t nbh, int64_t T, int blk, hipStream_t s) {
+    if (nbh < 0 || T < 0 || (blk && T % 32)) return -1;
     if (nbh * T == 0) return 0;
-    if (T <= 512) k_softmax_reg<8><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
-    else if (T <= 2048) k_softmax_reg<32><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
-    else k_softmax<<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T);
+    if (T <= 512) k_softmax_reg<8><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T, blk);
+    else if (T <= 2048) k_softmax_reg<32><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T, blk);
+    else k_softmax<<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T, blk);
     return ok();
 }
 
@@ -489,9 +497,11 @@ int attn_rowdot(const float* dO, const float* O, int64_t B, int64_t H, int64_t T
     return ok();
 }
 
-int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t T, float scale, hipStream_t s) {
+int softmax_bwd(const float* P, float* dP, const float* D, int64_t nbh, int64_t T, float scale, int blk,
+                hipStream_t s) {
+    if (blk && T % 32) return -1;
     if (nbh * T == 0) return 0;
-    k_softmax_bwd<<<dim3((unsigned)T, (unsigned)nbh), 256, 0, s>>>(P, dP, D, T, scale);
+    k_softmax_bwd<<<dim3((unsigned)T, (unsigned)nbh), 256, 0, s>>>(P, dP, D, T, scale, blk);
     return ok();
 }
 

@@ -57,16 +57,20 @@ mlb_status mlb_prim_rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, 
 /* Causal attention for B*H heads (model card: 12 heads x 64, context 2,048):
  * S = (q.k)*RN(1/sqrt(hd)) for j <= i, P = softmax with MAX64/SUM64 and
  * e*(1/Z), O = G1024 over j <= i of P v. q,k,v point at head (0,0); head (b,h)
- * row t at ptr[(b*T+t)*ld + h*hd]. P [B*H,T,T] (j <= i written), O rows ldo. */
+ * row t at ptr[(b*T+t)*ld + h*hd]. P holds B*H matrices of T*T floats (only
+ * j <= i written): row-major when p_tiled = 0, else the training step's
+ * layout of 32x32 tiles (element (i,j) at ((i/32)*(T/32) + j/32)*1024 +
+ * (i%32)*32 + j%32; needs T % 32 == 0 and hd <= 64). O rows at stride ldo. */
 mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, const float* k,
-                                  const float* v, int64_t ld, float* P, float* O, int64_t ldo, void* hip_stream);
+                                  const float* v, int64_t ld, float* P, float* O, int64_t ldo, int p_tiled,
+                                  void* hip_stream);
 /* D = DOT64(dO,O); dP = dO.v; dS = (P*(dP-D))*scale; dq = dS k (j <= i);
  * dk = dS^T q, dv = P^T dO (i >= j). dq/dk/dv use the q layout.
  * ws: B*H*T*T + B*H*T floats. */
 mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, const float* k,
                                   const float* v, int64_t ld, const float* P, const float* O, const float* dO,
-                                  int64_t ldo, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
-                                  void* hip_stream);
+                                  int64_t ldo, float* dq, float* dk, float* dv, int p_tiled, void* ws,
+                                  size_t ws_bytes, void* hip_stream);
 
 /* SwiGLU (model card: SwiGLU, 2,048 wide): gu rows [g | u] of 2F, a = (g*sig(g))*u,
  * sig(x) = 1/(1+exp(-x)). Backward writes dgu [rows, 2F]. */

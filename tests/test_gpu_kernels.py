@@ -244,21 +244,23 @@ def test_rope(mlb):
         assert_bits(f"rope bwd={bwd}", host(xd), want)
 
 
-@pytest.mark.parametrize("BH,T,hd", [(2, 64, 8), (3, 300, 5), (2, 1100, 64)])
-def test_attention_fwd_bwd(mlb, BH, T, hd):
+@pytest.mark.parametrize("BH,T,hd,tiled", [(2, 64, 8, 0), (2, 64, 8, 1), (3, 300, 5, 0), (2, 1100, 64, 0),
+                                           (2, 1088, 64, 1), (3, 96, 5, 1)])
+def test_attention_fwd_bwd(mlb, BH, T, hd, tiled):
     rng = np.random.default_rng(T + hd)
     q, k, v, dO = (make(rng, (BH, T, hd)) for _ in range(4))
     P, O = empty(BH * T * T), empty(BH * T * hd)
     qd, kd, vd = dev(q), dev(k), dev(v)
-    mlb.attention_fwd(BH, 1, T, hd, qd, kd, vd, hd, P, O, hd)
+    mlb.attention_fwd(BH, 1, T, hd, qd, kd, vd, hd, P, O, hd, tiled=tiled)
     Po, Oo = oracle.attention_fwd(q, k, v)
     low = np.tril(np.ones((T, T), bool))
-    Pg = host(P).reshape(BH, T, T)
+    Pg = host(P)
+    Pg = mlb.tiled_to_dense(Pg, T) if tiled else Pg.reshape(BH, T, T)
     assert_bits("P", Pg[:, low], Po[:, low])
     assert_bits("O", host(O).reshape(BH, T, hd), Oo)
     dq, dk, dv = empty(BH * T * hd), empty(BH * T * hd), empty(BH * T * hd)
     ws = empty(BH * T * T + BH * T)
-    mlb.attention_bwd(BH, 1, T, hd, qd, kd, vd, hd, P, O, dev(dO), hd, dq, dk, dv, ws)
+    mlb.attention_bwd(BH, 1, T, hd, qd, kd, vd, hd, P, O, dev(dO), hd, dq, dk, dv, ws, tiled=tiled)
     dqo, dko, dvo = oracle.attention_bwd(q, k, v, Po, Oo, dO)
     assert_bits("dq", host(dq).reshape(BH, T, hd), dqo)
     assert_bits("dk", host(dk).reshape(BH, T, hd), dko)
