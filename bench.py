@@ -40,32 +40,68 @@ def flops_per_token(cfg: dict) -> float:
     return 6.0 * p_mm + 6.0 * L * d * (T + 1)
 
 
+# Source files whose change invalidates measured HBM traffic of a kernel family.
+_KERNEL_SOURCES = {"k_gemm": "mlb_gemm.hip", "k_tri_nt": "mlb_attn.hip"}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    import hashlib
+    csrc = os.path.join(ROOT, "bitwise_reproducible_fp32_amd", "csrc")
+    fam = kernel.split("<")[0].strip()
+    files = [_KERNEL_SOURCES.get(fam, "mlb_ops.hip"), "mlb_internal.hpp", "mlb_device.hpp"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, cfg_name: str) -> float | None:
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a
+    copy of known size), or None when there is none for this kernel and
+    workload or the kernel's source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{cfg_name}.md")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_source_digest(kernel)
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("traffic:"):
+                continue
+            f = dict(kv.split("=", 1) for kv in line[len("traffic:"):].split())
+            if f.get("kernel") == kernel.replace(" ", "") and f.get("source_sha256") == digest:
+                return float(f["bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(cfg_name: str, init: np.ndarray, seconds_hint: float) -> dict:
     """The oracle as it stands, on a bounded sample of the workload: one
-    forward+backward of a 1 x 512-token micro-batch of the same model, with
-    OpenMP across independent outputs on this host's cores. The rate is scaled
-    to tokens/s of the benchmark workload by FLOPs per token."""
+    forward+backward of a 2 x seq_len micro-batch of the same model (half the
+    workload's micro-batch, same window length), with OpenMP across independent
+    outputs on this host's cores. The rate is scaled to tokens/s of the
+    benchmark workload by FLOPs per token."""
     import oracle
     from bitwise_reproducible_fp32_amd import inputs as I
     cfg = I.make_config(cfg_name)
-    T = min(512, cfg["seq_len"])
-    scfg = dict(cfg, batch=1, seq_len=T)
+    T = cfg["seq_len"]
+    Bs = min(2, cfg["batch"])
+    scfg = dict(cfg, batch=Bs, seq_len=T)
     cores = min(16, len(os.sched_getaffinity(0)))
     oracle.set_threads(cores)
     m = oracle.Model(scfg, init)
     if cfg_name == "c0":
-        x, y = I.c0_batch(0, 1, T)
+        x, y = I.c0_batch(0, Bs, T)
     else:
-        w = I.zipf_ids(T + 1, cfg["vocab"], [9, 0])
-        x, y = w[:T], w[1:]
+        x, y = I.zipf_batch(scfg, 0)
     t0 = time.perf_counter()
     m.forward(x, y)
     m.backward()
     dt = time.perf_counter() - t0
-    sample_flops = flops_per_token(scfg) * T
+    sample_flops = flops_per_token(scfg) * Bs * T
     rate = sample_flops / dt
     return {"value": rate / flops_per_token(cfg), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle forward+backward of one 1x{T}-token micro-batch of the {cfg_name} model "
+            "sample": f"oracle forward+backward of one {Bs}x{T}-token micro-batch of the {cfg_name} model "
                       f"({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s), scaled by FLOPs per token of the workload",
             "gflops": rate / 1e9, "seconds": dt}
 
@@ -78,6 +114,9 @@ def main() -> int:
     ap.add_argument("--config", default="c4", choices=["c0", "c3", "c4"])
     ap.add_argument("--micro", type=int, default=0, help="micro-batches per step (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="before the run, negate a MIB-MiB float32 buffer into another (a plain streaming kernel of "
+                         "known traffic that scales the HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; the data-parallel path over several "
@@ -88,6 +127,16 @@ def main() -> int:
 
     import bitwise_reproducible_fp32_amd as mlb
     from bitwise_reproducible_fp32_amd import inputs as I
+
+    if a.copy_probe > 0:
+        n = a.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"# copy probe: {n * 4} bytes read, {n * 4} bytes written", file=sys.stderr, flush=True)
+        del src, dst
 
     cfg = I.make_config(a.config)
     if a.micro:
@@ -160,7 +209,8 @@ def main() -> int:
     mem_sites = {}
     for st in stats:
         if st["bytes"] > 0:
-            r = mem_sites.setdefault(st["site"], dict(ms=0.0, bytes=0.0, launches=0))
+            key = st["site"] if st["kernel"] == st["site"] else f'{st["site"]}:{st["kernel"]}'
+            r = mem_sites.setdefault(key, dict(ms=0.0, bytes=0.0, launches=0))
             r["ms"] += st["ms"]; r["bytes"] += st["bytes"]; r["launches"] += st["launches"]
 
     out = {
@@ -184,7 +234,7 @@ def main() -> int:
         "flops_per_token": fpt,
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": round(dom_achieved, 2),
                      "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_achieved / PEAK_FP32_TFLOPS, 4),
-                     "traffic": None, "avg_ms": round(dom_avg_ms, 4), "launches": dom["launches"],
+                     "traffic": measured_traffic(dom_name, a.config), "avg_ms": round(dom_avg_ms, 4), "launches": dom["launches"],
                      "flops_per_launch": dom["flops"] / dom["launches"], "sites": sorted(dom["sites"])},
         "contractions": {"ms_share": round(gemm_ms / total_ms, 4) if total_ms else None,
                          "tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 2) if gemm_ms else None},

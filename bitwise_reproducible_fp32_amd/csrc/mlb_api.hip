@@ -380,32 +380,29 @@ void stat_resolve(mlb_model* M) {
     M->pending.clear();
 }
 
-// Algorithmic FLOPs of a contraction: 2 per valid (i, j, k) triple.
-double gemm_flops(const mlb::GemmDesc& g) {
-    double pairs = 0.0;
-    const double M = (double)g.M, N = (double)g.N, K = (double)g.K;
-    if (g.outmask) {            // j <= i, all k
-        const double m = std::min(M, N);
-        pairs = (m * (m + 1) / 2 + (M - m) * N) * K;
-    } else if (g.krange == 1) { // k <= i
-        const double m = std::min(M, K);
-        pairs = (m * (m + 1) / 2 + (M - m) * K) * N;
-    } else if (g.krange == 2) { // k >= i
-        const double m = std::min(M, K);
-        pairs = (m * (m + 1) / 2) * N;
-    } else {
-        pairs = M * N * K;
-    }
-    return 2.0 * pairs * (double)g.batch;
+// Every dispatch of a contraction is timed on its own, with its own FLOPs.
+struct GemmStatCtx {
+    mlb_model* M;
+    const char* site;
+    int64_t ev;
+};
+void gemm_stat_begin(void* c) {
+    auto* x = static_cast<GemmStatCtx*>(c);
+    x->ev = stat_begin(x->M);
+}
+void gemm_stat_end(void* c, const char* kernel, double flops, double bytes) {
+    auto* x = static_cast<GemmStatCtx*>(c);
+    stat_end(x->M, x->ev, x->site, kernel, flops, bytes);
 }
 
 mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
     mlb::GemmPlan p;
     p.scratch = M->split;
     p.scratch_floats = M->split_n;
-    const int64_t ev = stat_begin(M);
-    const int r = mlb::gemm(g, p, M->stream);
-    stat_end(M, ev, site, mlb::gemm_last_kernel(), gemm_flops(g), 0.0);
+    GemmStatCtx ctx{M, site, -1};
+    mlb::LaunchTrace tr;
+    tr.ctx = &ctx; tr.begin = gemm_stat_begin; tr.end = gemm_stat_end;
+    const int r = mlb::gemm(g, p, M->stream, M->stats_on ? &tr : nullptr);
     if (r != 0) return fail(MLB_E_DEVICE, "contraction %ldx%ldx%ld failed (%d)", (long)g.M, (long)g.N, (long)g.K, r);
     return MLB_OK;
 }
@@ -463,8 +460,8 @@ mlb_status forward(mlb_model* M) {
         OP("rmsnorm_fwd", f4 * (2 * N * d + N + d),
            mlb::rmsnorm_fwd(M->h[l], M->p + M->o_w1[l], N, d, M->cfg.rms_eps, M->xn1[l], M->r1[l], st));
         RUN("qkv_fwd", lin(N, 3 * d, d, M->xn1[l], d, true, M->p + M->o_qkv[l], d, true, M->qkv[l], 3 * d, 0));
-        OP("rope_fwd", f4 * 4 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
-        OP("rope_fwd", f4 * 4 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+        OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+        OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
         // S = (q . k) * scale, j <= i
         TRI("attn_scores", T, hd, M->qkv[l], 3 * d, T * 3 * d, M->qkv[l] + d, 3 * d, T * 3 * d, M->P[l], 1,
             M->attn_scale);
@@ -541,8 +538,8 @@ mlb_status backward(mlb_model* M) {
         dk.B = M->qkv[l]; dk.ldb = 3 * d; dk.b_kc = false; dk.sBb = T * 3 * d; dk.sBh = hd;
         dk.C = M->dqkv + d; dk.ldc = 3 * d; dk.sCb = T * 3 * d; dk.sCh = hd;
         RUN("attn_dk", dk);
-        OP("rope_bwd", f4 * 4 * N * d, mlb::rope(M->dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
-        OP("rope_bwd", f4 * 4 * N * d, mlb::rope(M->dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(M->dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(M->dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
         RUN("qkv_dw", lin(3 * d, d, N, M->dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1));
         mlb::GemmDesc x1 = lin(N, d, 3 * d, M->dqkv, 3 * d, true, M->p + M->o_qkv[l], d, false, M->dxn, d, 0);
         x1.kseg = d;                       // segments [dq Wq, dk Wk, dv Wv]

@@ -26,6 +26,7 @@
 // dispatcher assigns workgroup w to XCD w mod 8), grouped 8 tile-rows deep
 // for L2 reuse of the B panel.
 #include <cstdio>
+#include <cstring>
 
 #include "mlb_device.hpp"
 #include "mlb_internal.hpp"
@@ -48,6 +49,10 @@ struct KArgs {
     float scale;
     float* part;
     int64_t tiles_m, tiles_n, ntiles;
+    // chunk >= 0: this launch runs only that 1024-chunk of a causal contraction
+    // over row tiles tm_lo.. (launched in chunk order; rows whose first chunk
+    // it is store, later chunks add to C)
+    int64_t chunk, tm_lo;
 };
 
 // Offset of element (r, c) of a matrix stored as 32x32 tiles, each 4 KiB
@@ -57,11 +62,11 @@ __device__ __forceinline__ int64_t blk_off(int64_t ld, int64_t r, int64_t c) {
     return (((r >> 5) * (ld >> 5) + (c >> 5)) << 10) + ((r & 31) << 5) + (c & 31);
 }
 
-__device__ __forceinline__ void epilogue_store(const KArgs& a, float* C, int64_t gi, int64_t gj, float v) {
+__device__ __forceinline__ void epilogue_store(const KArgs& a, int mode, float* C, int64_t gi, int64_t gj, float v) {
     float* p = C + gi * a.ldc + gj;
-    if (a.mode == 0) *p = v;
-    else if (a.mode == 1) *p = *p + v;
-    else if (a.mode == 2) *p = v * a.scale;
+    if (mode == 0) *p = v;
+    else if (mode == 1) *p = *p + v;
+    else if (mode == 2) *p = v * a.scale;
     else *p = a.R[gi * a.ldc + gj] + v;
 }
 
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     const int64_t tn = (logical % per_group) / gsize;
     // k <= i: later row tiles hold more work, so they are dispatched first
     const int64_t tmr = (KR == 1) ? a.tiles_m - 1 - tm : tm;
-    const int64_t i0 = tmr * MT, j0 = tn * NT;
+    const int64_t i0 = (tmr + a.tm_lo) * MT, j0 = tn * NT;
     if (a.outmask && j0 > i0 + MT - 1) return;   // whole tile above the diagonal: nothing to write
 
     const int64_t z = blockIdx.z, zb = z / a.H, zh = z % a.H;
@@ -113,6 +118,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
         kbeg = sg * a.kseg + ch * KC;
         kend = sg * a.kseg + ((ch + 1) * KC < a.kseg ? (ch + 1) * KC : a.kseg);
     }
+    if (a.chunk >= 0) {   // one chunk of a causal contraction (kseg == K)
+        kbeg = a.chunk * KC;
+        kend = (kbeg + KC < a.K) ? kbeg + KC : a.K;
+    }
+    // the row's first non-empty chunk applies the mode; later chunks add
+    // (k <= i: chunk 0 for every row; k >= i: the chunk holding row i)
+    const int64_t first_chunk = (KR == 2) ? i0 / KC : 0;
+    const int emode = (a.chunk < 0 || a.chunk == first_chunk) ? a.mode : 1;
     if (KR == 1) kend = (kend < i0 + MT) ? kend : i0 + MT;
     if (KR == 2) kbeg = (kbeg > i0) ? kbeg : i0;
     const int64_t kt0 = kbeg / KT, kt1 = (kend + KT - 1) / KT;
@@ -333,10 +346,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
                 if (gi < a.M && gj0 < a.N) part[gi * a.N + gj0] = v0[e];
                 if (gi < a.M && gj1 < a.N) part[gi * a.N + gj1] = v1[e];
             } else {
+                if (!valid && emode == 1) continue;   // no term in this chunk: unchanged
                 if (gi < a.M && gj0 < a.N && (!a.outmask || gj0 <= gi))
-                    epilogue_store(a, C, gi, gj0, valid ? v0[e] : 0.0f);
+                    epilogue_store(a, emode, C, gi, gj0, valid ? v0[e] : 0.0f);
                 if (gi < a.M && gj1 < a.N && (!a.outmask || gj1 <= gi))
-                    epilogue_store(a, C, gi, gj1, valid ? v1[e] : 0.0f);
+                    epilogue_store(a, emode, C, gi, gj1, valid ? v1[e] : 0.0f);
             }
         }
     };
@@ -386,7 +400,7 @@ __global__ __launch_bounds__(256) void k_gemm_simple(KArgs a, int a_kc, int b_kc
             total = have ? total + acc : acc;
             have = true;
         }
-    epilogue_store(a, C, i, j, have ? total : 0.0f);
+    epilogue_store(a, a.mode, C, i, j, have ? total : 0.0f);
 }
 
 // total = part[0] + part[1] + ... in chunk order, then the epilogue.
@@ -397,7 +411,7 @@ __global__ __launch_bounds__(256) void k_fold(const float* __restrict__ part, in
     if (idx >= MN) return;
     float t = part[idx];
     for (int64_t c = 1; c < nch; ++c) t = t + part[c * MN + idx];
-    epilogue_store(a, a.C, idx / N, idx % N, t);
+    epilogue_store(a, a.mode, a.C, idx / N, idx % N, t);
 }
 
 struct Cfg { int wm, wn; };
@@ -408,22 +422,27 @@ template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, int KT = 32, bool 
 void launch_t(const KArgs& a, bool vec, bool mc, dim3 grid, hipStream_t s) {
     std::snprintf(g_launched, sizeof g_launched, "k_gemm<%s, %s, %d, %d, %d, %d, %s, %s, %d, %s>",
                   AKC ? "true" : "false", BKC ? "true" : "false", WM, WN, RB, KR, vec ? "true" : "false",
-                  (KR != 0 || mc) ? "true" : "false", KT, ABLK ? "true" : "false");
-    if (KR != 0 || mc) {
+                  mc ? "true" : "false", KT, ABLK ? "true" : "false");
+    if (mc) {
         if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
         else k_gemm<AKC, BKC, WM, WN, RB, KR, false, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
     } else {
-        if (vec) k_gemm<AKC, BKC, WM, WN, RB, 0, true, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
-        else k_gemm<AKC, BKC, WM, WN, RB, 0, false, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
+        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
     }
 }
 
 // Tile configurations: 0 = 128x128 (2x2 waves of 64x64), 1 = 256x64 (4x1 waves
 // of 64x64), 2 = 128x64 (4x1 waves of 32x64; the causal ranges).
 // Returns false when no tiled instantiation exists for the combination.
-bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_t nsplit, hipStream_t s) {
-    const int64_t MT = cfg == 0 ? 128 : (cfg == 1 ? 256 : 128), NT = cfg == 0 ? 128 : 64;
-    a.tiles_m = (d.M + MT - 1) / MT;
+// tm_count >= 0 restricts the launch to row tiles [tm_lo, tm_lo + tm_count).
+int64_t tile_rows(int cfg) { return cfg == 1 ? 256 : 128; }
+
+bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_t nsplit, hipStream_t s,
+                  int64_t tm_lo = 0, int64_t tm_count = -1) {
+    const int64_t MT = tile_rows(cfg), NT = cfg == 0 ? 128 : 64;
+    a.tm_lo = tm_lo;
+    a.tiles_m = tm_count >= 0 ? tm_count : (d.M + MT - 1) / MT;
     a.tiles_n = (d.N + NT - 1) / NT;
     a.ntiles = a.tiles_m * a.tiles_n;
     const dim3 grid((unsigned)a.ntiles, (unsigned)nsplit, (unsigned)d.batch);
@@ -504,8 +523,37 @@ int64_t gemm_split_scratch(const GemmDesc& d, const GemmPlan& p) {
 
 const char* gemm_last_kernel() { return g_launched; }
 
-int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s) {
+double gemm_flops(const GemmDesc& d, int64_t kb, int64_t ke) {
+    kb = kb > 0 ? kb : 0;
+    ke = ke < d.K ? ke : d.K;
+    if (kb >= ke || d.M <= 0 || d.N <= 0) return 0.0;
+    double pairs = 0.0;
+    if (d.krange == 0 && !d.outmask) {
+        pairs = (double)d.M * (double)d.N * (double)(ke - kb);
+    } else {
+        for (int64_t i = 0; i < d.M; ++i) {
+            int64_t lo = kb, hi = ke;
+            if (d.krange == 1) hi = (i + 1 < hi) ? i + 1 : hi;
+            if (d.krange == 2) lo = (i > lo) ? i : lo;
+            if (lo >= hi) continue;
+            const int64_t cols = d.outmask ? ((i + 1 < d.N) ? i + 1 : d.N) : d.N;
+            pairs += (double)cols * (double)(hi - lo);
+        }
+    }
+    return 2.0 * pairs * (double)d.batch;
+}
+
+namespace {
+struct Traced {
+    const LaunchTrace* tr;
+    void begin() const { if (tr && tr->begin) tr->begin(tr->ctx); }
+    void end(double flops, double bytes) const { if (tr && tr->end) tr->end(tr->ctx, g_launched, flops, bytes); }
+};
+}  // namespace
+
+int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace* tr) {
     std::snprintf(g_launched, sizeof g_launched, "none");
+    const Traced t{tr};
     if (!desc_ok(d)) return -1;
     if (d.M == 0 || d.N == 0) return 0;
     KArgs a{};
@@ -513,12 +561,14 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s) {
     a.A = d.A; a.lda = d.lda; a.B = d.B; a.ldb = d.ldb; a.C = d.C; a.ldc = d.ldc; a.R = d.R;
     a.H = d.H; a.sAb = d.sAb; a.sAh = d.sAh; a.sBb = d.sBb; a.sBh = d.sBh; a.sCb = d.sCb; a.sCh = d.sCh;
     a.outmask = d.outmask; a.mode = d.mode; a.krange = d.krange; a.scale = d.scale;
-    a.split = 0; a.part = nullptr;
+    a.split = 0; a.part = nullptr; a.chunk = -1; a.tm_lo = 0;
     if (p.simple || d.K == 0) {
         const int64_t n = d.M * d.N;
         const dim3 grid((unsigned)((n + 255) / 256), 1, (unsigned)d.batch);
         std::snprintf(g_launched, sizeof g_launched, "k_gemm_simple");
+        t.begin();
         k_gemm_simple<<<grid, 256, 0, s>>>(a, d.a_kc ? 1 : 0, d.b_kc ? 1 : 0);
+        t.end(gemm_flops(d, 0, d.K), 0.0);
         return hipGetLastError() == hipSuccess ? 0 : -3;
     }
     // float4 loads need 16-byte alignment and a leading dimension that covers
@@ -538,20 +588,52 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s) {
         a.split = 1;
         a.part = p.scratch;
     }
+    // A causal contraction over several chunks runs one launch per chunk in
+    // chunk order, each over the row tiles that chunk touches: the row's first
+    // chunk stores, later ones add, which is the rule's left fold t0 + t1 + ...
+    // Only for mode 0 (an existing C would be added before the fold ends) and
+    // when every row's range is non-empty.
+    const int64_t nch = nchunks(d);
+    if (d.krange != 0 && nch > 1 && p.split != 0 && d.mode == 0 && !d.outmask &&
+        (d.krange == 1 || d.M <= d.K) && cfg == 2 && KC % tile_rows(cfg) == 0) {
+        const int64_t MT = tile_rows(cfg), tiles = (d.M + MT - 1) / MT;
+        for (int64_t c = 0; c < nch; ++c) {
+            int64_t lo, hi;   // row tiles with a non-empty range in chunk c
+            if (d.krange == 1) { lo = c * KC / MT; hi = tiles; }
+            else { lo = 0; const int64_t e = (c + 1) * KC < d.M ? (c + 1) * KC : d.M; hi = (e + MT - 1) / MT; }
+            if (lo >= hi) continue;
+            a.chunk = c;
+            t.begin();
+            if (!launch_tiled(d, a, cfg, vec, false, 1, s, lo, hi - lo)) return -1;
+            t.end(gemm_flops(d, c * KC, (c + 1) * KC), 0.0);
+            if (hipGetLastError() != hipSuccess) return -3;
+        }
+        return 0;
+    }
     // several chunks (or segments) per workgroup need the running total
-    const bool mc = !split && nchunks(d) > 1;
+    const bool mc = !split && nch > 1;
+    t.begin();
     if (!launch_tiled(d, a, cfg, vec, mc, nsplit, s)) {
         if (split) return -1;
         const int64_t n = d.M * d.N;
         const dim3 grid((unsigned)((n + 255) / 256), 1, (unsigned)d.batch);
         std::snprintf(g_launched, sizeof g_launched, "k_gemm_simple");
         k_gemm_simple<<<grid, 256, 0, s>>>(a, d.a_kc ? 1 : 0, d.b_kc ? 1 : 0);
+        t.end(gemm_flops(d, 0, d.K), 0.0);
         return hipGetLastError() == hipSuccess ? 0 : -3;
     }
+    t.end(gemm_flops(d, 0, d.K), 0.0);
     if (hipGetLastError() != hipSuccess) return -3;
     if (split) {
         const int64_t n = d.M * d.N;
+        char main_kernel[sizeof g_launched];
+        std::memcpy(main_kernel, g_launched, sizeof g_launched);
+        std::snprintf(g_launched, sizeof g_launched, "k_fold");
+        t.begin();
         k_fold<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p.scratch, nsplit, d.M, d.N, a);
+        // partials read, output written (and read when accumulating)
+        t.end(0.0, 4.0 * (double)n * (double)(nsplit + 1 + (d.mode == 1 || d.mode == 3 ? 1 : 0)));
+        std::memcpy(g_launched, main_kernel, sizeof g_launched);
         if (hipGetLastError() != hipSuccess) return -3;
     }
     return 0;

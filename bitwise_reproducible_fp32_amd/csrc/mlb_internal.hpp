@@ -51,12 +51,24 @@ struct GemmPlan {
     int simple = 0;           // 1: use the one-thread-per-output reference kernel
 };
 
+// Observer of single kernel dispatches: begin runs before a launch, end after
+// it with the kernel's name and its algorithmic work (FLOPs, 2 per valid
+// multiply-add; or minimal HBM bytes for a kernel without a contraction).
+struct LaunchTrace {
+    void* ctx = nullptr;
+    void (*begin)(void* ctx) = nullptr;
+    void (*end)(void* ctx, const char* kernel, double flops, double bytes) = nullptr;
+};
+
 // Floats of scratch the split path needs for d (0 when it would not split).
 int64_t gemm_split_scratch(const GemmDesc& d, const GemmPlan& p);
 // Returns 0, or a negative value when the description is invalid or unsupported.
-int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s);
-// Name of the contraction kernel the last gemm() call on this thread launched
-// (the split path also launches k_fold).
+// tr (may be null) sees every dispatch: the contraction launches (one, or one
+// per chunk of a causal range) and the split path's k_fold.
+int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace* tr = nullptr);
+// FLOPs of the valid multiply-adds of d with k in [kb, ke), all problems.
+double gemm_flops(const GemmDesc& d, int64_t kb, int64_t ke);
+// Name of the contraction kernel the last gemm() call on this thread launched.
 const char* gemm_last_kernel();
 
 // Lower triangle of a batched contraction over a short K (<= 64, one chunk):

@@ -31,7 +31,9 @@ extern "C" {
  * Launch choices that never change bits: tile (-1 auto, 0 128x128, 1 256x64,
  * 2 64x64; causal ranges need 2),
  * split (-1 auto, 0 off, 1 per-chunk partials folded by a second kernel; needs
- * ws of ceil(K/1024)*M*N floats), simple (1 = one thread per output). */
+ * ws of ceil(K/1024)*M*N floats; for a causal range in mode 0, -1 and 1 run
+ * one launch per chunk that stores the first chunk and adds the later ones,
+ * 0 keeps the running total in registers), simple (1 = one thread per output). */
 mlb_status mlb_prim_gemm(int64_t M, int64_t N, int64_t K, int64_t kseg, const float* A, int64_t lda, int a_kc,
                          const float* B, int64_t ldb, int b_kc, float* C, int64_t ldc, int krange, int outmask,
                          int mode, float scale, int64_t batch, int64_t heads, int64_t sAb, int64_t sAh,

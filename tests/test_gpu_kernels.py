@@ -149,8 +149,11 @@ def test_segments_and_modes(mlb):
 
 
 @pytest.mark.parametrize("krange", [1, 2])
-@pytest.mark.parametrize("T,hd", [(64, 8), (300, 5), (1100, 64)])
+@pytest.mark.parametrize("T,hd", [(64, 8), (300, 5), (1100, 64), (2300, 16)])
 def test_causal_ranges(mlb, krange, T, hd):
+    """Both launch forms of a causal contraction over several chunks (one
+    launch per chunk, or the running total in registers) and the one-thread
+    reference kernel give the oracle's bits."""
     rng = np.random.default_rng(T * krange)
     P = make(rng, (T, T))
     V = make(rng, (T, hd))
@@ -160,10 +163,10 @@ def test_causal_ranges(mlb, krange, T, hd):
     else:             # dV[j] = sum_{i>=j} P[i,j] dO[i]
         want = orc_contract(P, V, T, hd, T, T, False, hd, False, krange=2)
         a_kc = False
-    for simple in (0, 1):
-        C = empty(T * hd)
-        mlb.gemm(dev(P), dev(V), C, T, hd, T, T, a_kc, hd, False, hd, krange=krange, simple=simple)
-        assert_bits(f"krange {krange} simple {simple}", host(C).reshape(T, hd), want)
+    for simple, split in ((0, -1), (0, 0), (0, 1), (1, -1)):
+        C = dev(np.full(T * hd, np.nan, np.float32))
+        mlb.gemm(dev(P), dev(V), C, T, hd, T, T, a_kc, hd, False, hd, krange=krange, simple=simple, split=split)
+        assert_bits(f"krange {krange} simple {simple} split {split}", host(C).reshape(T, hd), want)
 
 
 def test_outmask_scores(mlb):
@@ -245,7 +248,7 @@ def test_rope(mlb):
 
 
 @pytest.mark.parametrize("BH,T,hd,tiled", [(2, 64, 8, 0), (2, 64, 8, 1), (3, 300, 5, 0), (2, 1100, 64, 0),
-                                           (2, 1088, 64, 1), (3, 96, 5, 1)])
+                                           (2, 1088, 64, 1), (3, 96, 5, 1), (1, 2080, 64, 1)])
 def test_attention_fwd_bwd(mlb, BH, T, hd, tiled):
     rng = np.random.default_rng(T + hd)
     q, k, v, dO = (make(rng, (BH, T, hd)) for _ in range(4))
