@@ -424,12 +424,14 @@ mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
 
 // Lower-triangle contraction over the head dimension for all B*H heads:
 // rows of A and B at stride ld (head h at column h*hd, batch b at b*sb).
+// P and D non-null: the softmax backward runs in the epilogue (C = dS).
 mlb_status run_tri(mlb_model* M, const char* site, int64_t T, int64_t hd, const float* A, int64_t lda, int64_t sAb,
-                   const float* B, int64_t ldb, int64_t sBb, float* C, int scaled, float scale) {
+                   const float* B, int64_t ldb, int64_t sBb, float* C, int scaled, float scale,
+                   const float* P = nullptr, const float* D = nullptr, float ds_scale = 0.0f) {
     const Sizes& s = M->s;
     const int64_t ev = stat_begin(M);
     const int r = mlb::tri_nt(T, hd, s.B * s.H, s.H, A, lda, sAb, hd, B, ldb, sBb, hd, C, T, s.H * T * T, T * T,
-                              scaled, scale, 1, M->stream);
+                              scaled, scale, 1, P, D, ds_scale, M->stream);
     stat_end(M, ev, site, "k_tri_nt", 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd,
              0.0);
     if (r != 0) return fail(MLB_E_DEVICE, "%s failed (%d)", site, r);
@@ -517,15 +519,15 @@ mlb_status backward(mlb_model* M) {
         RUN("wo_dx", lin(N, d, d, M->dh, d, true, M->p + M->o_wo[l], d, false, M->dO, d, 0));
         RUN("wo_dw", lin(d, d, N, M->dh, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
         OP("attn_rowdot", f4 * (2 * N * d + BH * T), mlb::attn_rowdot(M->dO, M->O[l], s.B, H, T, hd, d, M->Dv, st));
-        // dP = dO . v, j <= i
-        TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f);
+        // dS = (P * (dO . v - D)) * scale, j <= i (dP never reaches memory)
+        TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f, M->P[l], M->Dv,
+            M->attn_scale);
         mlb::GemmDesc dv = head_gemm(s);   // dv = P^T dO over i >= j
         dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.a_blk = true; dv.krange = 2;
         dv.A = M->P[l]; dv.lda = T; dv.a_kc = false; dv.sAb = H * T * T; dv.sAh = T * T;
         dv.B = M->dO; dv.ldb = d; dv.b_kc = false; dv.sBb = T * d; dv.sBh = hd;
         dv.C = M->dqkv + 2 * d; dv.ldc = 3 * d; dv.sCb = T * 3 * d; dv.sCh = hd;
         RUN("attn_dv", dv);
-        OP("softmax_bwd", f4 * 3 * tri, mlb::softmax_bwd(M->P[l], M->dP, M->Dv, BH, T, M->attn_scale, 1, st));
         mlb::GemmDesc dq = head_gemm(s);   // dq = dS k over j <= i
         dq.M = T; dq.N = hd; dq.K = T; dq.kseg = T; dq.a_blk = true; dq.krange = 1;
         dq.A = M->dP; dq.lda = T; dq.a_kc = true; dq.sAb = H * T * T; dq.sAh = T * T;
@@ -976,7 +978,7 @@ mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     const float scale = (float)(1.0 / std::sqrt((double)hd));
     if (hd <= 64) {
         if (mlb::tri_nt(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T, H * T * T, T * T, 1, scale,
-                        p_tiled, st))
+                        p_tiled, nullptr, nullptr, 0.0f, st))
             return fail(MLB_E_DEVICE, "scores");
     } else {
         mlb::GemmDesc sg;
@@ -1015,9 +1017,10 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     const float scale = (float)(1.0 / std::sqrt((double)hd));
     if (mlb::attn_rowdot(dO, O, B, H, T, hd, ldo, D, st)) return fail(MLB_E_DEVICE, "rowdot");
     if (hd <= 64) {
+        // dS directly: the softmax backward runs in the epilogue
         if (mlb::tri_nt(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T, H * T * T, T * T, 0, 1.0f,
-                        p_tiled, st))
-            return fail(MLB_E_DEVICE, "dP");
+                        p_tiled, P, D, scale, st))
+            return fail(MLB_E_DEVICE, "dS");
     } else {
         mlb::GemmDesc g;
         g.batch = B * H; g.H = H;
@@ -1034,7 +1037,7 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     gv.B = dO; gv.ldb = ldo; gv.b_kc = false; gv.sBb = T * ldo; gv.sBh = hd;
     gv.C = dv; gv.ldc = ld; gv.sCb = T * ld; gv.sCh = hd;
     if (mlb::gemm(gv, plan, st)) return fail(MLB_E_DEVICE, "dv");
-    if (mlb::softmax_bwd(P, dP, D, B * H, T, scale, p_tiled, st)) return fail(MLB_E_DEVICE, "softmax_bwd");
+    if (hd > 64 && mlb::softmax_bwd(P, dP, D, B * H, T, scale, p_tiled, st)) return fail(MLB_E_DEVICE, "softmax_bwd");
     mlb::GemmDesc gq;
     gq.batch = B * H; gq.H = H;
     gq.M = T; gq.N = hd; gq.K = T; gq.kseg = T; gq.krange = 1; gq.a_blk = p_tiled != 0;

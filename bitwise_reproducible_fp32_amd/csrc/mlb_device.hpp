@@ -83,6 +83,18 @@ __device__ __forceinline__ float sigmoid_p(float x) { return 1.0f / (1.0f + exp_
 
 __device__ __forceinline__ float max_keep(float a, float b) { return (b > a) ? b : a; }
 
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by
+// linear id. This maps the linear id of the whole grid (x fastest) to a
+// logical index such that each XCD runs one contiguous range of logical work,
+// so neighbouring tiles (and whole problems of a batch) share one L2. It is a
+// bijection on [0, total) and never changes what a tile computes.
+__device__ __forceinline__ int64_t xcd_logical_block() {
+    const int64_t L = (int64_t)blockIdx.x + (int64_t)gridDim.x * ((int64_t)blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+    const int64_t total = (int64_t)gridDim.x * gridDim.y * gridDim.z;
+    const int64_t xcd = L & 7, idx = L >> 3, base = total >> 3, rem = total & 7;
+    return xcd * base + (xcd < rem ? xcd : rem) + idx;
+}
+
 // Lane tree of the W64 rule; the result is valid in lane 0 and returned to all lanes.
 __device__ __forceinline__ float wave_tree_sum(float acc) {
 #pragma unroll

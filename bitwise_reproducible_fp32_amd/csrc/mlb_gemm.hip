@@ -70,8 +70,15 @@ __device__ __forceinline__ void epilogue_store(const KArgs& a, int mode, float* 
     else *p = a.R[gi * a.ldc + gj] + v;
 }
 
+// Single-chunk vector-load instances fit in 168 registers, three waves per
+// SIMD (the attention contractions gain most); the others keep the default so
+// that their running totals do not spill.
+template <bool VEC, bool MC>
+constexpr int gemm_waves_per_eu() { return (VEC && !MC) ? 3 : 1; }
+
 template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, bool VEC, bool MC, int KT, bool ABLK = false>
-__global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(gemm_waves_per_eu<VEC, MC>())))
+void k_gemm(KArgs a) {
     // Each wave owns RB 32-row blocks x 64 columns (two 32x32 MFMA blocks per
     // row block). MC: the contraction may span several 1024-chunks, so a
     // running total is kept beside the chunk accumulator.
@@ -91,10 +98,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     const int wm = wave % WM, wn = wave / WM;
     const int lk = lane >> 5, li = lane & 31;
 
-    // XCD-aware tile order, then grouped rows.
-    const int64_t w = blockIdx.x, nt = a.ntiles;
-    const int64_t xcd = w & 7, idx = w >> 3, base = nt >> 3, rem = nt & 7;
-    const int64_t logical = xcd * base + (xcd < rem ? xcd : rem) + idx;
+    // XCD-aware order over (tile, chunk, problem), problem slowest, then
+    // grouped tile rows inside a problem.
+    const int64_t lb = xcd_logical_block();
+    const int64_t gy = (lb / gridDim.x) % gridDim.y, gz = lb / ((int64_t)gridDim.x * gridDim.y);
+    const int64_t logical = lb % gridDim.x;
     constexpr int64_t GM = 8;
     const int64_t per_group = GM * a.tiles_n;
     const int64_t first_m = (logical / per_group) * GM;
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     const int64_t i0 = (tmr + a.tm_lo) * MT, j0 = tn * NT;
     if (a.outmask && j0 > i0 + MT - 1) return;   // whole tile above the diagonal: nothing to write
 
-    const int64_t z = blockIdx.z, zb = z / a.H, zh = z % a.H;
+    const int64_t z = gz, zb = z / a.H, zh = z % a.H;
     const float* __restrict__ A = a.A + zb * a.sAb + zh * a.sAh;
     const float* __restrict__ B = a.B + zb * a.sBb + zh * a.sBh;
     float* C = a.C + zb * a.sCb + zh * a.sCh;
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
     int64_t kbeg = 0, kend = a.K;
     if (a.split) {   // one chunk of the segment-major chunk list
         const int64_t per_seg = (a.kseg + KC - 1) / KC;
-        const int64_t sg = (int64_t)blockIdx.y / per_seg, ch = (int64_t)blockIdx.y % per_seg;
+        const int64_t sg = gy / per_seg, ch = gy % per_seg;
         kbeg = sg * a.kseg + ch * KC;
         kend = sg * a.kseg + ((ch + 1) * KC < a.kseg ? (ch + 1) * KC : a.kseg);
     }
@@ -336,21 +344,52 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm(KArgs a) {
         }
     }
 
+    // Epilogue of one 32-row block against the wave's two 32-column blocks.
+    // Interior blocks (all rows < M, all columns < N, no mask) store without a
+    // per-element branch; read-modify-write modes load every operand before
+    // the first store. Either way each element gets exactly the mode's one
+    // operation, so the bits do not depend on the path.
     auto store_pair = [&](const v16f& v0, const v16f& v1, int64_t bi, bool valid) {
+        const int mode = a.split ? 0 : emode;
+        if (!valid && mode == 1) return;   // no term in this chunk: unchanged
+        const int64_t gj0 = j0 + j0l, gj1 = j0 + j1l;
+        float* out = a.split ? a.part + gy * a.M * a.N : C;
+        const int64_t ld = a.split ? a.N : a.ldc;
+        const bool interior = bi + 32 <= a.M && j0 + NT <= a.N && (a.split || !a.outmask);
+        auto row = [&](int e) -> int64_t { return bi + 8 * (e >> 2) + 4 * lk + (e & 3); };
+        auto ok0 = [&](int64_t gi) { return interior || (gi < a.M && gj0 < a.N && (a.split || !a.outmask || gj0 <= gi)); };
+        auto ok1 = [&](int64_t gi) { return interior || (gi < a.M && gj1 < a.N && (a.split || !a.outmask || gj1 <= gi)); };
+        float x0[16], x1[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t gi = bi + 8 * (e >> 2) + 4 * lk + (e & 3);
-            const int64_t gj0 = j0 + j0l, gj1 = j0 + j1l;
-            if (a.split) {
-                float* part = a.part + (int64_t)blockIdx.y * a.M * a.N;
-                if (gi < a.M && gj0 < a.N) part[gi * a.N + gj0] = v0[e];
-                if (gi < a.M && gj1 < a.N) part[gi * a.N + gj1] = v1[e];
-            } else {
-                if (!valid && emode == 1) continue;   // no term in this chunk: unchanged
-                if (gi < a.M && gj0 < a.N && (!a.outmask || gj0 <= gi))
-                    epilogue_store(a, emode, C, gi, gj0, valid ? v0[e] : 0.0f);
-                if (gi < a.M && gj1 < a.N && (!a.outmask || gj1 <= gi))
-                    epilogue_store(a, emode, C, gi, gj1, valid ? v1[e] : 0.0f);
+        for (int e = 0; e < 16; ++e) { x0[e] = valid ? v0[e] : 0.0f; x1[e] = valid ? v1[e] : 0.0f; }
+        if (mode == 1 || mode == 3) {
+            const float* src = mode == 1 ? out : a.R;
+            float r0[16], r1[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = row(e);
+                r0[e] = ok0(gi) ? src[gi * ld + gj0] : 0.0f;
+                r1[e] = ok1(gi) ? src[gi * ld + gj1] : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { x0[e] = r0[e] + x0[e]; x1[e] = r1[e] + x1[e]; }
+        } else if (mode == 2) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { x0[e] = x0[e] * a.scale; x1[e] = x1[e] * a.scale; }
+        }
+        if (interior) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = row(e);
+                out[gi * ld + gj0] = x0[e];
+                out[gi * ld + gj1] = x1[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = row(e);
+                if (ok0(gi)) out[gi * ld + gj0] = x0[e];
+                if (ok1(gi)) out[gi * ld + gj1] = x1[e];
             }
         }
     };

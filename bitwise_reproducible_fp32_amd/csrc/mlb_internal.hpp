@@ -75,9 +75,11 @@ const char* gemm_last_kernel();
 // C(i,j) = t(i,j) (times scale when scaled) for j <= i < T, with
 // t(i,j) = fma chain over k of A[i*lda + k] * B[j*ldb + k] (mlb_attn.hip).
 // blk: C is stored in the tiled layout (ldc = T, a multiple of 32).
+// P and D non-null (scaled 0): softmax backward in the epilogue, C(i,j) =
+// (P(i,j) * (t(i,j) - D[z*T + i])) * ds_scale, with P laid out as C.
 int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
            const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
-           int scaled, float scale, int blk, hipStream_t s);
+           int scaled, float scale, int blk, const float* P, const float* D, float ds_scale, hipStream_t s);
 
 // Row and elementwise kernels (mlb_ops.hip). All return 0 or a negative value
 // on invalid sizes; they launch on stream s and never synchronise.
