@@ -149,8 +149,35 @@ void k_gemm(KArgs a) {
     const int64_t bi00 = i0 + r0, bi01 = i0 + r1;
 
     float ra[EA * W], rb[EB * W];
+    // Tiles whose rows, columns and K range are all in bounds load and store
+    // without per-element checks or masks (a uniform branch per K tile).
+    const bool rows_in = i0 + MT <= a.M, cols_in = j0 + NT <= a.N;
     auto load_global = [&](int64_t kt) {
         const int64_t k0 = kt * KT;
+        if (VEC && rows_in && cols_in && k0 + KT <= a.K) {
+#pragma unroll
+            for (int s = 0; s < EA; ++s) {
+                const int q = tid + s * NTHR;
+                int64_t gi, gk;
+                if (AKC) { gi = i0 + q / (KT / W); gk = k0 + (q % (KT / W)) * W; }
+                else { gk = k0 + q / (MT / W); gi = i0 + (q % (MT / W)) * W; }
+                const float4 v = ABLK ? *reinterpret_cast<const float4*>(A + blk_off(a.lda, AKC ? gi : gk, AKC ? gk : gi))
+                               : AKC ? *reinterpret_cast<const float4*>(A + gi * a.lda + gk)
+                                     : *reinterpret_cast<const float4*>(A + gk * a.lda + gi);
+                ra[s * 4 + 0] = v.x; ra[s * 4 + 1] = v.y; ra[s * 4 + 2] = v.z; ra[s * 4 + 3] = v.w;
+            }
+#pragma unroll
+            for (int s = 0; s < EB; ++s) {
+                const int q = tid + s * NTHR;
+                int64_t gj, gk;
+                if (BKC) { gj = j0 + q / (KT / W); gk = k0 + (q % (KT / W)) * W; }
+                else { gk = k0 + q / (NT / W); gj = j0 + (q % (NT / W)) * W; }
+                const float4 v = BKC ? *reinterpret_cast<const float4*>(B + gj * a.ldb + gk)
+                                     : *reinterpret_cast<const float4*>(B + gk * a.ldb + gj);
+                rb[s * 4 + 0] = v.x; rb[s * 4 + 1] = v.y; rb[s * 4 + 2] = v.z; rb[s * 4 + 3] = v.w;
+            }
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < EA; ++s) {
             const int q = tid + s * NTHR;
@@ -200,6 +227,35 @@ void k_gemm(KArgs a) {
     };
     auto store_lds = [&](int64_t kt) {
         const int64_t k0 = kt * KT;
+        if (VEC && k0 + KT <= a.K) {   // no K tail inside this tile: plain copies
+#pragma unroll
+            for (int s = 0; s < EA; ++s) {
+                const int q = tid + s * NTHR;
+                if (AKC) {
+                    const int i = q / (KT / W), k = (q % (KT / W)) * W;
+#pragma unroll
+                    for (int e = 0; e < W; ++e) As[i * ALD + k + e] = ra[s * W + e];
+                } else {
+                    const int k = q / (MT / W), i = (q % (MT / W)) * W;
+#pragma unroll
+                    for (int e = 0; e < W; ++e) As[k * ALD + i + e] = ra[s * W + e];
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < EB; ++s) {
+                const int q = tid + s * NTHR;
+                if (BKC) {
+                    const int j = q / (KT / W), k = (q % (KT / W)) * W;
+#pragma unroll
+                    for (int e = 0; e < W; ++e) Bs[j * BLD + k + e] = rb[s * W + e];
+                } else {
+                    const int k = q / (NT / W), j = (q % (NT / W)) * W;
+#pragma unroll
+                    for (int e = 0; e < W; ++e) Bs[k * BLD + j + e] = rb[s * W + e];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < EA; ++s) {
             const int q = tid + s * NTHR;
@@ -502,6 +558,14 @@ bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_
             case 2: launch_t<false, true, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
         }
     }
+    if (d.krange == 0 && cfg == 2) {
+        switch (key) {
+            case 3: launch_t<true, true, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
+            case 1: launch_t<true, false, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
+            case 0: launch_t<false, false, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
+            case 2: launch_t<false, true, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
+        }
+    }
     // causal ranges; a tiled A (32x32 blocks, the attention probability layout)
     // is read as whole contiguous 4 KiB tiles
     if (d.krange == 1 && key == 1 && cfg == 2) {
@@ -616,10 +680,16 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     bool vec = aligned16(d.A) && aligned16(d.B) && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
                d.sAb % 4 == 0 && d.sAh % 4 == 0 && d.sBb % 4 == 0 && d.sBh % 4 == 0;
     vec = vec && (d.a_kc ? up4(d.K) <= d.lda : up4(d.M) <= d.lda) && (d.b_kc ? up4(d.K) <= d.ldb : up4(d.N) <= d.ldb);
-    // 128x128 tiles in general, 256x64 for 64-wide outputs, one-wave 64x64 tiles
-    // for causal ranges (their work per row tile grows along the diagonal)
-    int cfg = p.tile >= 0 ? p.tile : (d.krange != 0 ? 2 : (d.N <= 64 ? 1 : 0));
     const bool split = want_split(d, p);
+    // 128x128 tiles in general; 128x64 when 128x128 tiles would not fill the
+    // chip once (fewer workgroups than 256 CUs x 3 resident); 256x64 for
+    // 64-wide outputs; 128x64 for causal ranges (their work per row tile grows
+    // along the diagonal)
+    int cfg = p.tile;
+    if (cfg < 0) {
+        const int64_t wg128 = ((d.M + 127) / 128) * ((d.N + 127) / 128) * (split ? nchunks(d) : 1) * d.batch;
+        cfg = d.krange != 0 ? 2 : (d.N <= 64 ? 1 : (wg128 < 768 ? 2 : 0));
+    }
     int64_t nsplit = 1;
     if (split) {
         nsplit = nchunks(d);

@@ -29,7 +29,7 @@ extern "C" {
  * writes j <= i only. batch = number of problems, heads divides batch, problem
  * z = zb*heads + zh offsets A by zb*sAb + zh*sAh (same for B, C).
  * Launch choices that never change bits: tile (-1 auto, 0 128x128, 1 256x64,
- * 2 64x64; causal ranges need 2),
+ * 2 128x64; causal ranges need 2),
  * split (-1 auto, 0 off, 1 per-chunk partials folded by a second kernel; needs
  * ws of ceil(K/1024)*M*N floats; for a causal range in mode 0, -1 and 1 run
  * one launch per chunk that stores the first chunk and adds the later ones,

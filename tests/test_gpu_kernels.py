@@ -110,7 +110,7 @@ def test_contraction_odd_shapes(mlb, M, K, N, layout):
     lda = K if a_kc else M
     ldb = K if b_kc else N
     want = orc_contract(A, B, M, N, K, lda, a_kc, ldb, b_kc)
-    for tile in (0, 1):
+    for tile in (0, 1, 2):
         C = empty(M * N)
         mlb.gemm(dev(A), dev(B), C, M, N, K, lda, a_kc, ldb, b_kc, N, tile=tile)
         assert_bits(f"{layout} tile {tile}", host(C).reshape(M, N), want)
