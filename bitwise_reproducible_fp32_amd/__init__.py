@@ -53,7 +53,7 @@ vp, i64, i32, f32, sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t
 _SIGS = {
     "mlb_param_count": (i64, [C.POINTER(Config)]),
     "mlb_workspace_bytes": (i32, [C.POINTER(Config), C.POINTER(sz)]),
-    "mlb_init": (i32, [C.POINTER(Config), vp, vp, sz, vp, C.POINTER(vp)]),
+    "mlb_init": (i32, [C.POINTER(Config), C.c_uint64, vp, vp, sz, vp, C.POINTER(vp)]),
     "mlb_forward_loss": (i32, [vp, vp, vp, C.POINTER(f32)]),
     "mlb_backward": (i32, [vp]),
     "mlb_adamw_step": (i32, [vp, f32]),
@@ -129,22 +129,27 @@ def _stream(stream=None):
 class Model:
     """One training state on the current GPU; the arena is a torch uint8 tensor."""
 
-    def __init__(self, cfg: dict, init_params: np.ndarray, device: str = "cuda:0", stream=None):
+    def __init__(self, cfg: dict, init_params: np.ndarray | None = None, device: str = "cuda:0", stream=None,
+                 seed: int = 0):
+        """init_params: step-0 parameters in canonical order, or None to draw
+        them from seed with the library's own generator."""
         import torch
         self.cfg = dict(cfg)
         self._c = config(cfg)
         self.n = param_count(cfg)
-        init = np.ascontiguousarray(init_params, dtype=np.float32)
-        if init.size != self.n:
-            raise ValueError(f"init has {init.size} values, the model {self.n}")
+        init = None
+        if init_params is not None:
+            init = np.ascontiguousarray(init_params, dtype=np.float32)
+            if init.size != self.n:
+                raise ValueError(f"init has {init.size} values, the model {self.n}")
         torch.cuda.set_device(torch.device(device))
         nbytes = workspace_bytes(cfg)
         self.arena = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
         off = (-self.arena.data_ptr()) % 256
         self._stream_obj = stream if stream is not None else torch.cuda.current_stream(device)
         h = vp()
-        check(lib().mlb_init(C.byref(self._c), init.ctypes.data, self.arena.data_ptr() + off, nbytes,
-                             self._stream_obj.cuda_stream, C.byref(h)))
+        check(lib().mlb_init(C.byref(self._c), C.c_uint64(seed), None if init is None else init.ctypes.data,
+                             self.arena.data_ptr() + off, nbytes, self._stream_obj.cuda_stream, C.byref(h)))
         self.h = h
 
     def close(self) -> None:

@@ -18,6 +18,7 @@
 #include <cstring>
 #include <map>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "../../include/mlb.h"
@@ -309,6 +310,42 @@ void offsets(mlb_model* M) {
     M->offOut = s.tied ? M->offE : o;
 }
 
+// Step-0 parameters from a seed (callers that pass none). SplitMix64 in its
+// counter form: output i is the variant-13 finaliser applied to seed + (i + 1)
+// * 0x9E3779B97F4A7C15. Parameter k takes outputs 2k and 2k+1 through the
+// Box-Muller transform in binary64; norm gains are 1 + 0.02 z, the rest 0.02 z,
+// rounded once. Host threads split the index range (each value depends on k
+// only).
+uint64_t splitmix_at(uint64_t seed, uint64_t i) {
+    uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+std::vector<float> seeded_params(const mlb_model* M, uint64_t seed) {
+    const Sizes& s = M->s;
+    std::vector<float> out((size_t)s.P);
+    std::vector<char> gain((size_t)s.P, 0);
+    for (int64_t l = 0; l < s.L; ++l)
+        for (int64_t c = 0; c < s.d; ++c) gain[(size_t)(M->o_w1[l] + c)] = gain[(size_t)(M->o_w2[l] + c)] = 1;
+    auto fill = [&](int64_t lo, int64_t hi) {
+        for (int64_t k = lo; k < hi; ++k) {
+            const uint64_t r1 = splitmix_at(seed, 2 * (uint64_t)k), r2 = splitmix_at(seed, 2 * (uint64_t)k + 1);
+            const double u1 = (double)((r1 >> 11) + 1) * 0x1p-53;
+            const double u2 = (double)(r2 >> 11) * 0x1p-53;
+            const double z = std::sqrt(-2.0 * std::log(u1)) * std::cos(6.283185307179586 * u2);
+            const double w = 0.02 * z;
+            out[(size_t)k] = gain[(size_t)k] ? (float)(1.0 + w) : (float)w;
+        }
+    };
+    const int64_t nthr = 8, per = (s.P + nthr - 1) / nthr;
+    std::vector<std::thread> th;
+    for (int64_t t = 0; t < nthr; ++t) th.emplace_back(fill, t * per, std::min(s.P, (t + 1) * per));
+    for (auto& x : th) x.join();
+    return out;
+}
+
 // RoPE table: cos/sin of t * theta^(-2i/hd), binary64 on the host, rounded.
 void rope_table_host(int64_t T, int64_t hd, float theta, std::vector<float>& c, std::vector<float>& sn) {
     const int64_t h2 = hd / 2;
@@ -585,10 +622,10 @@ mlb_status mlb_workspace_bytes(const mlb_config* cfg, size_t* bytes) {
     return MLB_OK;
 }
 
-mlb_status mlb_init(const mlb_config* cfg, const float* init, void* arena, size_t arena_bytes, void* stream,
-                    mlb_model** out) {
+mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init, void* arena, size_t arena_bytes,
+                    void* stream, mlb_model** out) {
     std::string why;
-    if (!out || !init || !arena) return fail(MLB_E_INVALID_ARG, "null argument");
+    if (!out || !arena) return fail(MLB_E_INVALID_ARG, "null argument");
     *out = nullptr;
     if (!cfg_valid(cfg, &why)) return fail(MLB_E_INVALID_ARG, "%s", why.c_str());
     if (!cfg_supported(cfg, &why)) return fail(MLB_E_UNSUPPORTED, "%s", why.c_str());
@@ -617,6 +654,11 @@ mlb_status mlb_init(const mlb_config* cfg, const float* init, void* arena, size_
     if (hipHostMalloc(reinterpret_cast<void**>(&M->host_stage), 64, hipHostMallocDefault) != hipSuccess) {
         delete M;
         return fail(MLB_E_DEVICE, "pinned staging buffer");
+    }
+    std::vector<float> drawn;
+    if (!init) {
+        drawn = seeded_params(M, seed);
+        init = drawn.data();
     }
     std::vector<float> c, sn;
     rope_table_host(M->s.T, M->s.hd, cfg->rope_theta, c, sn);

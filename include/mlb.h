@@ -69,13 +69,20 @@ int64_t mlb_param_count(const mlb_config* cfg);
 mlb_status mlb_workspace_bytes(const mlb_config* cfg, size_t* bytes);
 
 /* Creates a model on the current HIP device. init_params_host: host float32
- * array of mlb_param_count(cfg) values (step-0 parameters), read during the
- * call. dev_arena: caller-owned device memory of arena_bytes, 256-byte aligned,
- * untouched by anything else while the model lives. hip_stream: a hipStream_t
- * (may be null). Moments and the gradient accumulator start at +0, step 0.
- * Refuses a device that is not gfx950 (MLB_E_UNSUPPORTED). */
-mlb_status mlb_init(const mlb_config* cfg, const float* init_params_host, void* dev_arena, size_t arena_bytes,
-                    void* hip_stream, mlb_model** out);
+ * array of mlb_param_count(cfg) values (step-0 parameters, canonical order),
+ * read during the call; or NULL, and the step-0 parameters are drawn from seed
+ * (model card "Training" table: N(0, 0.02) weights, norm gains 1 + N(0, 0.02))
+ * by the profile's own generator: parameter k takes SplitMix64 outputs 2k and
+ * 2k+1 of the stream started at seed (Steele, Lea and Flood 2014), u1 =
+ * (first >> 11 plus 1) * 2^-53, u2 = (second >> 11) * 2^-53, z = sqrt(-2 log u1)
+ * * cos(2 pi u2) in binary64 (Box-Muller), value 0.02 z (gains 1 + 0.02 z)
+ * rounded once to binary32. dev_arena: caller-owned device memory of
+ * arena_bytes, 256-byte aligned, untouched by anything else while the model
+ * lives. hip_stream: a hipStream_t (may be null). Moments and the gradient
+ * accumulator start at +0, step 0. Refuses a device that is not gfx950
+ * (MLB_E_UNSUPPORTED). */
+mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init_params_host, void* dev_arena,
+                    size_t arena_bytes, void* hip_stream, mlb_model** out);
 
 /* Forward pass and loss of one micro-batch: d_inputs and d_targets are device
  * int32 arrays of batch*seq_len ids (row-major [batch, seq_len]), read before

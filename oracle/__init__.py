@@ -46,6 +46,21 @@ def cfg_struct(cfg: dict) -> Cfg:
                *[float(cfg[n]) for n, t in Cfg._fields_ if t is C.c_float])
 
 
+def splitmix64(seed: int, n: int) -> np.ndarray:
+    """The first n SplitMix64 outputs from seed (uint64)."""
+    out = np.empty(n, np.uint64)
+    lib().orc_splitmix64(C.c_uint64(seed), n, out.ctypes.data_as(C.POINTER(C.c_uint64)))
+    return out
+
+
+def seed_params(cfg: dict, seed: int) -> np.ndarray:
+    """Step-0 parameters drawn from seed by the profile's own generator."""
+    c = cfg_struct(cfg)
+    out = np.empty(lib().orc_param_count(C.byref(c)), np.float32)
+    lib().orc_seed_params(C.byref(c), C.c_uint64(seed), out)
+    return out
+
+
 def load(path: str = LIB_PATH):
     global _lib
     if _lib is not None and path == LIB_PATH:
@@ -85,6 +100,8 @@ def load(path: str = LIB_PATH):
         "orc_adamw": (None, [F32P, F32P, F32P, F32P, i64, f32, f32, f32, f32, f32, f32, f32]),
         "orc_sha256": (None, [U8P, i64, U8P]),
         "orc_param_count": (i64, [C.POINTER(Cfg)]),
+        "orc_splitmix64": (None, [C.c_uint64, i64, C.POINTER(C.c_uint64)]),
+        "orc_seed_params": (None, [C.POINTER(Cfg), C.c_uint64, F32P]),
         "orc_model_new": (C.c_void_p, [C.POINTER(Cfg), F32P]),
         "orc_model_free": (None, [C.c_void_p]),
         "orc_model_forward": (i32, [C.c_void_p, I32P, I32P, C.POINTER(C.c_float)]),

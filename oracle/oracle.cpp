@@ -846,6 +846,41 @@ int64_t orc_param_count(const orc_cfg* cfg) {
     return make_layout(*cfg).nparams;
 }
 
+void orc_splitmix64(uint64_t seed, int64_t n, uint64_t* out) {
+    uint64_t state = seed;
+    for (int64_t i = 0; i < n; ++i) {
+        state += 0x9E3779B97F4A7C15ull;
+        uint64_t z = state;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        out[i] = z ^ (z >> 31);
+    }
+}
+
+void orc_seed_params(const orc_cfg* cfg, uint64_t seed, float* out) {
+    if (!cfg || !cfg_ok(*cfg) || !out) return;
+    const Layout L = make_layout(*cfg);
+    const int64_t d = cfg->d_model;
+    // which canonical positions are norm gains
+    std::vector<char> gain((size_t)L.nparams, 0);
+    for (int l = 0; l < cfg->n_layers; ++l)
+        for (int64_t c = 0; c < d; ++c) { gain[(size_t)(L.w1[l] + c)] = 1; gain[(size_t)(L.w2[l] + c)] = 1; }
+    const double two_pi = 6.283185307179586;   // binary64 nearest to 2 pi
+    const double two_m53 = 1.0 / 9007199254740992.0;
+    uint64_t pair[2];
+    uint64_t state_seed = seed;
+    for (int64_t k = 0; k < L.nparams; ++k) {
+        orc_splitmix64(state_seed, 2, pair);        // outputs 2k and 2k+1
+        state_seed += 2 * 0x9E3779B97F4A7C15ull;
+        const double u1 = (double)((pair[0] >> 11) + 1) * two_m53;
+        const double u2 = (double)(pair[1] >> 11) * two_m53;
+        const double radius = std::sqrt(-2.0 * std::log(u1));
+        const double z = radius * std::cos(two_pi * u2);
+        const double w = 0.02 * z;
+        out[k] = gain[(size_t)k] ? (float)(1.0 + w) : (float)w;
+    }
+}
+
 void* orc_model_new(const orc_cfg* cfg, const float* init) {
     if (!cfg || !cfg_ok(*cfg) || !init) return nullptr;
     Model* M = new Model();

@@ -129,6 +129,18 @@ typedef struct orc_cfg {
     float rope_theta, rms_eps, beta1, beta2, adam_eps, weight_decay;
 } orc_cfg;
 int64_t orc_param_count(const orc_cfg* cfg);
+/* The first n outputs of SplitMix64 started at seed (Steele, Lea and Flood,
+ * "Fast splittable pseudorandom number generators", 2014): the state advances
+ * by the golden gamma 0x9E3779B97F4A7C15 and each output is the state passed
+ * through the variant-13 finaliser. */
+void orc_splitmix64(uint64_t seed, int64_t n, uint64_t* out);
+/* Step-0 parameters from a seed, for a caller that passes none: parameter k of
+ * the canonical order takes SplitMix64 outputs 2k and 2k+1; u1 = (first >> 11
+ * plus 1) * 2^-53 in (0, 1], u2 = (second >> 11) * 2^-53; the Box-Muller
+ * transform (1958) in binary64 gives z = sqrt(-2 log u1) * cos(2 pi u2); norm
+ * gains take 1 + 0.02 z, every other parameter 0.02 z, each rounded once to
+ * binary32. out holds orc_param_count(cfg) floats. */
+void orc_seed_params(const orc_cfg* cfg, uint64_t seed, float* out);
 void* orc_model_new(const orc_cfg* cfg, const float* init_params);
 void orc_model_free(void* m);
 /* Forward and loss of one micro-batch; stores activations. Returns -1 (and sets

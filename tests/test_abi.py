@@ -79,6 +79,10 @@ def test_abi_version_checked(mlb):
 
 def test_null_arguments_refused(mlb):
     L = mlb.lib()
+    c = mlb.config(I.make_config("c0"))
+    h = C.c_void_p()
+    assert L.mlb_init(C.byref(c), 1, None, None, 0, None, C.byref(h)) == -1   # no arena
+    assert L.mlb_init(C.byref(c), 1, None, None, 0, None, None) == -1         # no handle slot
     assert L.mlb_backward(None) == -1
     assert L.mlb_adamw_step(None, 1.0) == -1
     n = C.c_size_t()

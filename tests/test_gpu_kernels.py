@@ -97,7 +97,8 @@ def orc_contract(A, B, M, N, K, lda, a_kc, ldb, b_kc, kseg=0, krange=0, outmask=
                        scale=scale, krange=krange, outmask=outmask).reshape(M, N)
 
 
-SHAPES = [(1, 1, 1), (37, 767, 5), (129, 3, 257), (200, 2100, 130), (64, 64, 64), (300, 1030, 70)]
+SHAPES = [(1, 1, 1), (37, 767, 5), (129, 3, 257), (200, 2100, 130), (64, 64, 64), (300, 1030, 70), (200, 2100, 132),
+          (136, 1500, 68)]
 
 
 @pytest.mark.parametrize("M,K,N", SHAPES)
