@@ -114,6 +114,9 @@ def main() -> int:
     ap.add_argument("--config", default="c4", choices=["c0", "c3", "c4"])
     ap.add_argument("--micro", type=int, default=0, help="micro-batches per step (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap", type=int, default=0, choices=[0, 1],
+                    help="run the backward weight-gradient work on the library's second stream (1), or everything "
+                         "on one stream (0, default: per-kernel times then measure each kernel alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="before the run, negate a MIB-MiB float32 buffer into another (a plain streaming kernel of "
                          "known traffic that scales the HBM byte counters)")
@@ -146,6 +149,7 @@ def main() -> int:
     init = I.init_params(cfg)
     torch.cuda.set_device(0)
     model = mlb.Model(cfg, init)
+    model.set_overlap(bool(a.overlap))
     nsteps = a.warmup + a.steps
     xs = np.empty((nsteps, S, B * T), np.int32)
     ys = np.empty_like(xs)
@@ -228,7 +232,7 @@ def main() -> int:
         "data": "synthetic (seeded Zipf(1.1) token ids, N(0,0.02) init)",
         "config": {"workload": f"{a.config}: {I.param_count(cfg):,}-param decoder, {S} micro-batches of "
                                f"{B}x{T} tokens per step", "tokens_per_step": tokens, "micro_batches": S,
-                   "batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+                   "batch": B, "seq_len": T, "parallelism": "none (1 GPU)", "stream_overlap": bool(a.overlap)},
         "tflops": round(tflops, 2),
         "pct_fp32_peak": round(100 * tflops / PEAK_FP32_TFLOPS, 2),
         "flops_per_token": fpt,

@@ -62,6 +62,7 @@ _SIGS = {
     "mlb_read": (i32, [vp, i32, vp, sz]),
     "mlb_read_stage": (i32, [vp, i32, i32, vp, sz, C.POINTER(sz)]),
     "mlb_step": (C.c_uint64, [vp]),
+    "mlb_set_overlap": (i32, [vp, i32]),
     "mlb_stats_enable": (i32, [vp, i32]),
     "mlb_stats_read": (i32, [vp, C.POINTER(Stat), i32, C.POINTER(i32)]),
     "mlb_destroy": (i32, [vp]),
@@ -201,6 +202,10 @@ class Model:
     @property
     def step(self) -> int:
         return int(lib().mlb_step(self.h))
+
+    def set_overlap(self, on: bool) -> None:
+        """Backward weight-gradient work on the library's second stream (default on)."""
+        check(lib().mlb_set_overlap(self.h, int(bool(on))))
 
     def stats_enable(self, on: bool = True) -> None:
         check(lib().mlb_stats_enable(self.h, int(on)))

@@ -215,10 +215,25 @@ struct StatAgg {
     double ms = 0, flops = 0, bytes = 0;
 };
 
+// Activation-gradient buffers shared by the caller's stream and the library's
+// side stream (which runs the weight-gradient work of the backward pass). The
+// main stream overwrites a slot only after the side stream's last reader of it
+// has finished (per-slot event).
+struct Ring {
+    std::vector<float*> buf;
+    std::vector<hipEvent_t> ev;
+    std::vector<char> pending;
+};
+
 struct mlb_model {
     mlb_config cfg;
     Sizes s;
-    hipStream_t stream;
+    hipStream_t stream;        // the caller's stream: every call is ordered on it
+    hipStream_t side = nullptr;
+    hipStream_t cur = nullptr; // the stream the op being enqueued runs on
+    bool overlap = true;       // backward weight-gradient work on the side stream
+    std::vector<hipEvent_t> sync_pool;
+    size_t sync_next = 0;
     int device;
     // parameter offsets (floats)
     int64_t offE, offOut;
@@ -232,7 +247,8 @@ struct mlb_model {
     float* loss_rows;
     std::vector<float*> h, xn1, r1, qkv, P, O, hmid, xn2, r2, gu, a;   // h has L+1 entries
     float* logits;
-    float *dh, *dA, *dgu, *dxn, *dO, *dqkv, *dP, *Dv, *gE, *split, *dwpart;
+    Ring dh, dgu, dxn, dqkv;
+    float *dA, *dO, *dP, *Dv, *gE, *split, *split_side, *dwpart;
     int64_t split_n;
     uint64_t* keys;
     float* host_stage;   // pinned, 64 bytes
@@ -247,6 +263,36 @@ struct mlb_model {
 };
 
 namespace {
+
+// The side stream (default priority, not synchronising with the null stream),
+// the pool of ordering events and one event per ring slot.
+mlb_status make_streams(mlb_model* M) {
+    if (hipStreamCreateWithFlags(&M->side, hipStreamNonBlocking) != hipSuccess)
+        return fail(MLB_E_DEVICE, "side stream");
+    M->sync_pool.assign(64, nullptr);
+    for (hipEvent_t& e : M->sync_pool)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return fail(MLB_E_DEVICE, "event");
+    for (Ring* r : {&M->dh, &M->dgu, &M->dxn, &M->dqkv}) {
+        r->ev.assign(r->buf.size(), nullptr);
+        r->pending.assign(r->buf.size(), 0);
+        for (hipEvent_t& e : r->ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return fail(MLB_E_DEVICE, "event");
+    }
+    M->cur = M->stream;
+    return MLB_OK;
+}
+
+void release_streams(mlb_model* M) {
+    if (M->side) (void)hipStreamSynchronize(M->side);
+    for (hipEvent_t e : M->sync_pool)
+        if (e) (void)hipEventDestroy(e);
+    for (Ring* r : {&M->dh, &M->dgu, &M->dxn, &M->dqkv})
+        for (hipEvent_t e : r->ev)
+            if (e) (void)hipEventDestroy(e);
+    if (M->side) (void)hipStreamDestroy(M->side);
+    M->side = nullptr;
+    M->sync_pool.clear();
+}
 
 size_t carve(mlb_model* M, char* base) {
     const Sizes& s = M->s;
@@ -279,17 +325,22 @@ size_t carve(mlb_model* M, char* base) {
         M->a[l] = c.take<float>(s.N * s.F);
     }
     M->logits = c.take<float>(s.N * s.ldV);
-    M->dh = c.take<float>(s.N * s.d);
+    auto ring = [&](Ring& r, int n, int64_t floats) {
+        r.buf.resize(n);
+        for (int i = 0; i < n; ++i) r.buf[i] = c.take<float>(floats);
+    };
+    ring(M->dh, 4, s.N * s.d);
     M->dA = c.take<float>(s.N * s.F);
-    M->dgu = c.take<float>(s.N * 2 * s.F);
-    M->dxn = c.take<float>(s.N * s.d);
+    ring(M->dgu, 2, s.N * 2 * s.F);
+    ring(M->dxn, 4, s.N * s.d);
     M->dO = c.take<float>(s.N * s.d);
-    M->dqkv = c.take<float>(s.N * 3 * s.d);
+    ring(M->dqkv, 2, s.N * 3 * s.d);
     M->dP = c.take<float>(s.B * s.H * s.T * s.T);
     M->Dv = c.take<float>(s.B * s.H * s.T);
     M->gE = s.tied ? c.take<float>(s.V * s.d) : nullptr;
     M->split_n = split_floats(s);
     M->split = c.take<float>(M->split_n > 0 ? M->split_n : 1);
+    M->split_side = c.take<float>(M->split_n > 0 ? M->split_n : 1);
     M->dwpart = c.take<float>(((s.N + KCH - 1) / KCH) * s.d);
     M->keys = c.take<uint64_t>(2 * MAX_TOKENS);
     return c.off + ALIGN;
@@ -377,8 +428,8 @@ mlb::GemmDesc lin(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, 
 }
 
 // ------------------------------------------------------------ launch stats
-// Optional per-launch timing with HIP events on the model's stream, grouped by
-// call site, with each launch's algorithmic work (FLOPs of the contraction's
+// Optional per-launch timing with HIP events on the stream the launch runs on
+// (the caller's or the side stream), grouped by call site, with each launch's algorithmic work (FLOPs of the contraction's
 // valid pairs, or the minimal HBM bytes of a row/elementwise kernel).
 int64_t stat_begin(mlb_model* M) {
     if (!M->stats_on) return -1;
@@ -389,7 +440,7 @@ int64_t stat_begin(mlb_model* M) {
     } else {
         if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return -1;
     }
-    if (hipEventRecord(e0, M->stream) != hipSuccess) return -1;
+    if (hipEventRecord(e0, M->cur) != hipSuccess) return -1;
     StatRec r;
     r.e0 = e0; r.e1 = e1;
     M->pending.push_back(r);
@@ -399,7 +450,7 @@ int64_t stat_begin(mlb_model* M) {
 void stat_end(mlb_model* M, int64_t idx, const char* site, const char* kernel, double flops, double bytes) {
     if (idx < 0) return;
     StatRec& r = M->pending[(size_t)idx];
-    (void)hipEventRecord(r.e1, M->stream);
+    (void)hipEventRecord(r.e1, M->cur);
     r.site = site; r.kernel = kernel; r.flops = flops; r.bytes = bytes;
 }
 
@@ -434,12 +485,12 @@ void gemm_stat_end(void* c, const char* kernel, double flops, double bytes) {
 
 mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
     mlb::GemmPlan p;
-    p.scratch = M->split;
+    p.scratch = (M->overlap && M->cur == M->side) ? M->split_side : M->split;   // one split scratch per stream
     p.scratch_floats = M->split_n;
     GemmStatCtx ctx{M, site, -1};
     mlb::LaunchTrace tr;
     tr.ctx = &ctx; tr.begin = gemm_stat_begin; tr.end = gemm_stat_end;
-    const int r = mlb::gemm(g, p, M->stream, M->stats_on ? &tr : nullptr);
+    const int r = mlb::gemm(g, p, M->cur, M->stats_on ? &tr : nullptr);
     if (r != 0) return fail(MLB_E_DEVICE, "contraction %ldx%ldx%ld failed (%d)", (long)g.M, (long)g.N, (long)g.K, r);
     return MLB_OK;
 }
@@ -468,7 +519,7 @@ mlb_status run_tri(mlb_model* M, const char* site, int64_t T, int64_t hd, const 
     const Sizes& s = M->s;
     const int64_t ev = stat_begin(M);
     const int r = mlb::tri_nt(T, hd, s.B * s.H, s.H, A, lda, sAb, hd, B, ldb, sBb, hd, C, T, s.H * T * T, T * T,
-                              scaled, scale, 1, P, D, ds_scale, M->stream);
+                              scaled, scale, 1, P, D, ds_scale, M->cur);
     stat_end(M, ev, site, "k_tri_nt", 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd,
              0.0);
     if (r != 0) return fail(MLB_E_DEVICE, "%s failed (%d)", site, r);
@@ -492,6 +543,7 @@ mlb::GemmDesc head_gemm(const Sizes& s) {
 mlb_status forward(mlb_model* M) {
     const Sizes& s = M->s;
     hipStream_t st = M->stream;
+    M->cur = st;
     const int64_t N = s.N, d = s.d, F = s.F, T = s.T, H = s.H, hd = s.hd, BH = s.B * s.H;
     const double f4 = 4.0, tri = (double)BH * (double)T * (double)(T + 1) / 2.0;
     OP("embed_gather", f4 * 2 * N * d, mlb::gather_rows(M->ids, M->p + M->offE, s.V, d, N, M->h[0], M->err, st));
@@ -529,74 +581,162 @@ mlb_status forward(mlb_model* M) {
     return MLB_OK;
 }
 
+// Cross-stream ordering: `to` waits for everything enqueued on `from` so far.
+mlb_status stream_wait(mlb_model* M, hipStream_t from, hipStream_t to) {
+    hipEvent_t e = M->sync_pool[M->sync_next];
+    M->sync_next = (M->sync_next + 1) % M->sync_pool.size();
+    if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess)
+        return fail(MLB_E_DEVICE, "stream ordering event");
+    return MLB_OK;
+}
+
+// The caller's stream is about to overwrite slot k of a ring.
+mlb_status ring_claim(mlb_model* M, Ring& r, int k) {
+    if (r.pending[k]) {
+        if (hipStreamWaitEvent(M->stream, r.ev[k], 0) != hipSuccess) return fail(MLB_E_DEVICE, "ring wait");
+        r.pending[k] = 0;
+    }
+    return MLB_OK;
+}
+
+// The side stream has enqueued its (last) reader of slot k.
+mlb_status ring_read(mlb_model* M, Ring& r, int k) {
+    if (!M->overlap) return MLB_OK;   // one stream: program order suffices
+    if (hipEventRecord(r.ev[k], M->side) != hipSuccess) return fail(MLB_E_DEVICE, "ring event");
+    r.pending[k] = 1;
+    return MLB_OK;
+}
+
+#define CHK(x)                                  \
+    do {                                        \
+        mlb_status st_ = (x);                   \
+        if (st_ != MLB_OK) return st_;          \
+    } while (0)
+
+// The backward pass runs on two streams. The caller's stream carries the
+// chain that produces each layer's input gradient; the side stream carries
+// the work that only feeds the gradient accumulator G (the weight-gradient
+// contractions, the norm gains, the embedding scatter), each started once its
+// inputs exist. Each G entry still receives exactly one addition per
+// micro-batch, in call order (one side stream), so the bits do not depend on
+// how the two streams interleave. The side stream joins the caller's stream at
+// the end.
 mlb_status backward(mlb_model* M) {
     const Sizes& s = M->s;
-    hipStream_t st = M->stream;
+    const bool two = M->overlap;
+    hipStream_t st = M->stream, ss = two ? M->side : M->stream;
     const int64_t N = s.N, d = s.d, F = s.F, T = s.T, H = s.H, hd = s.hd, BH = s.B * s.H;
-    const double f4 = 4.0, tri = (double)BH * (double)T * (double)(T + 1) / 2.0;
+    const double f4 = 4.0;
     const float* dl = M->logits;
-    // head: dh = dl W_out (K = V); W_out gradient = dl^T h_L (K = N), folded into G
-    RUN("head_dx", lin(N, d, s.V, dl, s.ldV, true, M->p + M->offOut, d, false, M->dh, d, 0));
+    auto on_main = [&]() { M->cur = st; };
+    auto to_side = [&]() -> mlb_status {   // the side stream sees everything the main stream did so far
+        M->cur = ss;
+        return two ? stream_wait(M, st, ss) : MLB_OK;
+    };
+    Ring &DH = M->dh, &DGU = M->dgu, &DXN = M->dxn, &DQKV = M->dqkv;
+
+    // head: dh = dl W_out (K = V); W_out gradient = dl^T h_L (K = N)
+    CHK(to_side());
     if (s.tied) RUN("head_dw", lin(s.V, d, N, dl, s.ldV, false, M->h[s.L], d, false, M->gE, d, 0));
     else RUN("head_dw", lin(s.V, d, N, dl, s.ldV, false, M->h[s.L], d, false, M->G + M->offOut, d, 1));
+    on_main();
+    int kh = 0;
+    CHK(ring_claim(M, DH, kh));
+    RUN("head_dx", lin(N, d, s.V, dl, s.ldV, true, M->p + M->offOut, d, false, DH.buf[kh], d, 0));
     for (int64_t l = s.L - 1; l >= 0; --l) {
+        const int kg = (int)(l % 2), kx2 = (int)(2 * (l % 2)), kx1 = kx2 + 1, kq = (int)(l % 2);
+        float* dh0 = DH.buf[kh];
         // MLP branch
-        RUN("down_dx", lin(N, F, d, M->dh, d, true, M->p + M->o_wd[l], F, false, M->dA, F, 0));
-        RUN("down_dw", lin(d, F, N, M->dh, d, false, M->a[l], F, false, M->G + M->o_wd[l], F, 1));
-        OP("swiglu_bwd", f4 * 5 * N * F, mlb::swiglu_bwd(M->dA, M->gu[l], N, F, M->dgu, st));
-        RUN("gu_dw", lin(2 * F, d, N, M->dgu, 2 * F, false, M->xn2[l], d, false, M->G + M->o_gu[l], d, 1));
-        mlb::GemmDesc x2 = lin(N, d, 2 * F, M->dgu, 2 * F, true, M->p + M->o_gu[l], d, false, M->dxn, d, 0);
+        RUN("down_dx", lin(N, F, d, dh0, d, true, M->p + M->o_wd[l], F, false, M->dA, F, 0));
+        CHK(to_side());
+        RUN("down_dw", lin(d, F, N, dh0, d, false, M->a[l], F, false, M->G + M->o_wd[l], F, 1));
+        CHK(ring_read(M, DH, kh));
+        on_main();
+        CHK(ring_claim(M, DGU, kg));
+        OP("swiglu_bwd", f4 * 5 * N * F, mlb::swiglu_bwd(M->dA, M->gu[l], N, F, DGU.buf[kg], st));
+        CHK(to_side());
+        RUN("gu_dw", lin(2 * F, d, N, DGU.buf[kg], 2 * F, false, M->xn2[l], d, false, M->G + M->o_gu[l], d, 1));
+        CHK(ring_read(M, DGU, kg));
+        on_main();
+        CHK(ring_claim(M, DXN, kx2));
+        mlb::GemmDesc x2 = lin(N, d, 2 * F, DGU.buf[kg], 2 * F, true, M->p + M->o_gu[l], d, false, DXN.buf[kx2], d, 0);
         x2.kseg = F;                       // segments [dg Wg, du Wu]
         RUN("gu_dx", x2);
+        CHK(to_side());
         OP("rmsnorm_dw", f4 * (2 * N * d + N + d),
-           mlb::rmsnorm_bwd_dw(M->dxn, M->hmid[l], M->r2[l], N, d, M->dwpart, M->G + M->o_w2[l], 1, st));
+           mlb::rmsnorm_bwd_dw(DXN.buf[kx2], M->hmid[l], M->r2[l], N, d, M->dwpart, M->G + M->o_w2[l], 1, ss));
+        CHK(ring_read(M, DXN, kx2));
+        on_main();
+        const int kh1 = (kh + 1) % 4;
+        CHK(ring_claim(M, DH, kh1));
+        float* dh1 = DH.buf[kh1];
         OP("rmsnorm_dx", f4 * (4 * N * d + N + d),
-           mlb::rmsnorm_bwd_dx(M->dxn, M->hmid[l], M->p + M->o_w2[l], M->r2[l], N, d, M->dh, 1, st));
+           mlb::rmsnorm_bwd_dx(DXN.buf[kx2], M->hmid[l], M->p + M->o_w2[l], M->r2[l], N, d, dh0, dh1, st));
         // attention branch
-        RUN("wo_dx", lin(N, d, d, M->dh, d, true, M->p + M->o_wo[l], d, false, M->dO, d, 0));
-        RUN("wo_dw", lin(d, d, N, M->dh, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
+        RUN("wo_dx", lin(N, d, d, dh1, d, true, M->p + M->o_wo[l], d, false, M->dO, d, 0));
+        CHK(to_side());
+        RUN("wo_dw", lin(d, d, N, dh1, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
+        CHK(ring_read(M, DH, kh1));
+        on_main();
         OP("attn_rowdot", f4 * (2 * N * d + BH * T), mlb::attn_rowdot(M->dO, M->O[l], s.B, H, T, hd, d, M->Dv, st));
         // dS = (P * (dO . v - D)) * scale, j <= i (dP never reaches memory)
         TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f, M->P[l], M->Dv,
             M->attn_scale);
+        CHK(ring_claim(M, DQKV, kq));
+        float* dqkv = DQKV.buf[kq];
         mlb::GemmDesc dv = head_gemm(s);   // dv = P^T dO over i >= j
         dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.a_blk = true; dv.krange = 2;
         dv.A = M->P[l]; dv.lda = T; dv.a_kc = false; dv.sAb = H * T * T; dv.sAh = T * T;
         dv.B = M->dO; dv.ldb = d; dv.b_kc = false; dv.sBb = T * d; dv.sBh = hd;
-        dv.C = M->dqkv + 2 * d; dv.ldc = 3 * d; dv.sCb = T * 3 * d; dv.sCh = hd;
+        dv.C = dqkv + 2 * d; dv.ldc = 3 * d; dv.sCb = T * 3 * d; dv.sCh = hd;
         RUN("attn_dv", dv);
         mlb::GemmDesc dq = head_gemm(s);   // dq = dS k over j <= i
         dq.M = T; dq.N = hd; dq.K = T; dq.kseg = T; dq.a_blk = true; dq.krange = 1;
         dq.A = M->dP; dq.lda = T; dq.a_kc = true; dq.sAb = H * T * T; dq.sAh = T * T;
         dq.B = M->qkv[l] + d; dq.ldb = 3 * d; dq.b_kc = false; dq.sBb = T * 3 * d; dq.sBh = hd;
-        dq.C = M->dqkv; dq.ldc = 3 * d; dq.sCb = T * 3 * d; dq.sCh = hd;
+        dq.C = dqkv; dq.ldc = 3 * d; dq.sCb = T * 3 * d; dq.sCh = hd;
         RUN("attn_dq", dq);
         mlb::GemmDesc dk = head_gemm(s);   // dk = dS^T q over i >= j
         dk.M = T; dk.N = hd; dk.K = T; dk.kseg = T; dk.a_blk = true; dk.krange = 2;
         dk.A = M->dP; dk.lda = T; dk.a_kc = false; dk.sAb = H * T * T; dk.sAh = T * T;
         dk.B = M->qkv[l]; dk.ldb = 3 * d; dk.b_kc = false; dk.sBb = T * 3 * d; dk.sBh = hd;
-        dk.C = M->dqkv + d; dk.ldc = 3 * d; dk.sCb = T * 3 * d; dk.sCh = hd;
+        dk.C = dqkv + d; dk.ldc = 3 * d; dk.sCb = T * 3 * d; dk.sCh = hd;
         RUN("attn_dk", dk);
-        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(M->dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
-        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(M->dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
-        RUN("qkv_dw", lin(3 * d, d, N, M->dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1));
-        mlb::GemmDesc x1 = lin(N, d, 3 * d, M->dqkv, 3 * d, true, M->p + M->o_qkv[l], d, false, M->dxn, d, 0);
+        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        CHK(to_side());
+        RUN("qkv_dw", lin(3 * d, d, N, dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1));
+        CHK(ring_read(M, DQKV, kq));
+        on_main();
+        CHK(ring_claim(M, DXN, kx1));
+        mlb::GemmDesc x1 = lin(N, d, 3 * d, dqkv, 3 * d, true, M->p + M->o_qkv[l], d, false, DXN.buf[kx1], d, 0);
         x1.kseg = d;                       // segments [dq Wq, dk Wk, dv Wv]
         RUN("qkv_dx", x1);
+        CHK(to_side());
         OP("rmsnorm_dw", f4 * (2 * N * d + N + d),
-           mlb::rmsnorm_bwd_dw(M->dxn, M->h[l], M->r1[l], N, d, M->dwpart, M->G + M->o_w1[l], 1, st));
+           mlb::rmsnorm_bwd_dw(DXN.buf[kx1], M->h[l], M->r1[l], N, d, M->dwpart, M->G + M->o_w1[l], 1, ss));
+        CHK(ring_read(M, DXN, kx1));
+        on_main();
+        const int kh2 = (kh1 + 1) % 4;
+        CHK(ring_claim(M, DH, kh2));
         OP("rmsnorm_dx", f4 * (4 * N * d + N + d),
-           mlb::rmsnorm_bwd_dx(M->dxn, M->h[l], M->p + M->o_w1[l], M->r1[l], N, d, M->dh, 1, st));
+           mlb::rmsnorm_bwd_dx(DXN.buf[kx1], M->h[l], M->p + M->o_w1[l], M->r1[l], N, d, dh1, DH.buf[kh2], st));
+        kh = kh2;
     }
     // embedding rows in token order (tied: on top of the head gradient, then folded)
+    CHK(to_side());
     if (s.tied) {
         OP("embed_scatter", f4 * 3 * N * d,
-           mlb::embed_scatter(M->ids, M->dh, N, d, s.V, M->gE, M->gE, 0, M->keys, st));
-        OP("embed_fold", f4 * 3 * s.V * d, mlb::add_inplace(M->G + M->offE, M->gE, s.V * d, st));
+           mlb::embed_scatter(M->ids, DH.buf[kh], N, d, s.V, M->gE, M->gE, 0, M->keys, ss));
+        OP("embed_fold", f4 * 3 * s.V * d, mlb::add_inplace(M->G + M->offE, M->gE, s.V * d, ss));
     } else {
         OP("embed_scatter", f4 * 3 * N * d,
-           mlb::embed_scatter(M->ids, M->dh, N, d, s.V, nullptr, M->G + M->offE, 1, M->keys, st));
+           mlb::embed_scatter(M->ids, DH.buf[kh], N, d, s.V, nullptr, M->G + M->offE, 1, M->keys, ss));
     }
+    // join: the caller's stream continues after all side work
+    on_main();
+    if (two) CHK(stream_wait(M, ss, st));
+    for (Ring* r : {&DH, &DGU, &DXN, &DQKV}) std::fill(r->pending.begin(), r->pending.end(), 0);
     return MLB_OK;
 }
 
@@ -655,6 +795,13 @@ mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init, voi
         delete M;
         return fail(MLB_E_DEVICE, "pinned staging buffer");
     }
+    if (make_streams(M) != MLB_OK) {
+        const mlb_status rc = MLB_E_DEVICE;
+        release_streams(M);
+        (void)hipHostFree(M->host_stage);
+        delete M;
+        return rc;
+    }
     std::vector<float> drawn;
     if (!init) {
         drawn = seeded_params(M, seed);
@@ -676,6 +823,7 @@ mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init, voi
     }
     step(hipStreamSynchronize(st), "init sync");
     if (rc != MLB_OK) {
+        release_streams(M);
         (void)hipHostFree(M->host_stage);
         delete M;
         return rc;
@@ -727,6 +875,7 @@ mlb_status mlb_adamw_step(mlb_model* M, float lr) {
     HIPCHK(hipSetDevice(M->device));
     const uint64_t t = M->step + 1;
     const float bc1 = bias_corr(M->cfg.beta1, t), bc2 = bias_corr(M->cfg.beta2, t);
+    M->cur = M->stream;
     OP("adamw", 4.0 * 8 * (double)M->s.P,
        mlb::adamw(M->p, M->G, M->m, M->v, M->s.P, lr, M->cfg.beta1, M->cfg.beta2, M->cfg.adam_eps,
                   M->cfg.weight_decay, bc1, bc2, M->stream));
@@ -892,10 +1041,20 @@ mlb_status mlb_destroy(mlb_model* M) {
     if (!M) return MLB_OK;
     (void)hipSetDevice(M->device);
     (void)hipStreamSynchronize(M->stream);
+    release_streams(M);
     stat_resolve(M);
     for (hipEvent_t e : M->free_events) (void)hipEventDestroy(e);
     (void)hipHostFree(M->host_stage);
     delete M;
+    return MLB_OK;
+}
+
+mlb_status mlb_set_overlap(mlb_model* M, int on) {
+    if (!M) return fail(MLB_E_INVALID_ARG, "null model");
+    if (M->have_fwd) return fail(MLB_E_STATE, "a forward is pending its backward");
+    HIPCHK(hipSetDevice(M->device));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    M->overlap = on != 0;
     return MLB_OK;
 }
 
@@ -989,7 +1148,7 @@ mlb_status mlb_prim_rmsnorm_bwd(const float* dy, const float* x, const float* w,
     const size_t need = (size_t)((rows + KCH - 1) / KCH) * (size_t)d * 4;
     if (ws_bytes < need || (!ws && need)) return fail(MLB_E_ARENA_TOO_SMALL, "rmsnorm_bwd needs %zu bytes", need);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (mlb::rmsnorm_bwd_dx(dy, x, w, r, rows, d, dx, 0, st) ||
+    if (mlb::rmsnorm_bwd_dx(dy, x, w, r, rows, d, nullptr, dx, st) ||
         mlb::rmsnorm_bwd_dw(dy, x, r, rows, d, static_cast<float*>(ws), dw, 0, st))
         return fail(MLB_E_INVALID_ARG, "rmsnorm_bwd");
     return MLB_OK;

@@ -87,9 +87,10 @@ int gather_rows(const int32_t* ids, const float* table, int64_t V, int64_t d, in
                 int* err, hipStream_t s);
 int rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float eps, float* y, float* r,
                 hipStream_t s);
-// dx = rmsnorm backward; written as out = out + dx when accumulate, else out = dx.
+// dx = rmsnorm backward; written as out = base + dx (base may be out itself),
+// or out = dx when base is null.
 int rmsnorm_bwd_dx(const float* dy, const float* x, const float* w, const float* r, int64_t rows,
-                   int64_t d, float* out, int accumulate, hipStream_t s);
+                   int64_t d, const float* base, float* out, hipStream_t s);
 // Gain gradient: per column the contraction over rows of dy * (x * r), chunks of
 // 1024 rows. part must hold ceil(rows/1024)*d floats. mode 0 dw = t, 1 dw = dw + t.
 int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows, int64_t d, float* part,

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x
 // xh = x * r; gw = dy * w; c = DOT64(gw, xh) / d; dx = r * (gw - xh * c).
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict__ dy, const float* __restrict__ x,
                                                         const float* __restrict__ w, const float* __restrict__ r,
-                                                        int64_t rows, int64_t d, float* out, int accumulate) {
+                                                        int64_t rows, int64_t d, const float* base, float* out) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
@@ -77,11 +77,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict_
     }
     const float cc = wave_tree_sum(acc) / (float)d;
     float* o = out + row * d;
+    const float* b = base ? base + row * d : nullptr;
     for (int64_t c = lane; c < d; c += 64) {
         const float xh = xr[c] * rr;
         const float gw = dr[c] * w[c];
         const float dx = rr * (gw - (xh * cc));
-        o[c] = accumulate ? o[c] + dx : dx;
+        o[c] = b ? b[c] + dx : dx;
     }
 }
 
@@ -452,10 +453,10 @@ int rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float e
 }
 
 int rmsnorm_bwd_dx(const float* dy, const float* x, const float* w, const float* r, int64_t rows, int64_t d,
-                   float* out, int accumulate, hipStream_t s) {
+                   const float* base, float* out, hipStream_t s) {
     if (rows < 0 || d <= 0) return -1;
     if (rows == 0) return 0;
-    k_rmsnorm_bwd_dx<<<blocks(rows, 4), 256, 0, s>>>(dy, x, w, r, rows, d, out, accumulate);
+    k_rmsnorm_bwd_dx<<<blocks(rows, 4), 256, 0, s>>>(dy, x, w, r, rows, d, base, out);
     return ok();
 }
 

@@ -13,8 +13,9 @@
  * cannot be met is refused by name instead of falling back).
  *
  * Memory: the caller owns one device arena (mlb_workspace_bytes) and the HIP
- * stream; the library owns the handle and a 64-byte pinned host staging buffer.
- * Every call enqueues on the caller's stream. mlb_forward_loss, mlb_save,
+ * stream; the library owns the handle, a 64-byte pinned host staging buffer and
+ * one side stream (see mlb_set_overlap). Every call is ordered on the caller's
+ * stream. mlb_forward_loss, mlb_save,
  * mlb_load and mlb_read synchronise that stream; the others do not.
  * A handle is not thread-safe. Errors are returned as negative mlb_status
  * values; mlb_last_error_message() (thread-local) gives the detail.
@@ -120,6 +121,17 @@ mlb_status mlb_read(const mlb_model* m, mlb_which which, void* host_dst, size_t 
  * 9 g|u, 10 SwiGLU output, 11 final hidden, 12 d-logits, 13 per-row losses).
  * *count receives the element count; host_dst may be NULL to query it. */
 mlb_status mlb_read_stage(const mlb_model* m, int stage, int layer, void* host_dst, size_t bytes, size_t* count);
+
+/* Stream overlap of the backward pass (default on). When on, the work that
+ * only feeds the gradient accumulator (weight-gradient contractions, norm-gain
+ * gradients, the embedding scatter) runs on a library-owned second stream of
+ * default priority, concurrently with the input-gradient chain on the caller's
+ * stream, and joins the caller's stream before mlb_backward returns; off runs
+ * everything on the caller's stream. The bits are the same either way (each
+ * accumulator entry receives one addition per micro-batch, in call order).
+ * Per-launch statistics of overlapping kernels include each other's time.
+ * MLB_E_STATE between a forward and its backward. Synchronises the stream. */
+mlb_status mlb_set_overlap(mlb_model* m, int on);
 
 /* Launch statistics (this library's own tracing). When enabled, every kernel
  * launch of the step is bracketed by HIP events on the model's stream and

@@ -32,10 +32,11 @@ def sha(a) -> str:
     return oracle.sha256(np.ascontiguousarray(a).tobytes())
 
 
-def run_gpu(name, cfg, steps, model=None, start=1, data_name=None):
+def run_gpu(name, cfg, steps, model=None, start=1, data_name=None, overlap=True):
     import bitwise_reproducible_fp32_amd as mlb
     data_name = data_name or name
     m = model or mlb.Model(cfg, I.init_params(cfg))
+    m.set_overlap(overlap)
     recs = []
     for s in range(start, start + steps):
         losses = []
@@ -79,9 +80,12 @@ def test_c0_first_step_stages_match_live_oracle():
         assert_bits(name, g.read(w), o.read(w))
 
 
-def test_c0_four_steps_bit_exact():
+@pytest.mark.parametrize("overlap", [True, False])
+def test_c0_four_steps_bit_exact(overlap):
+    """Both backward schedules (weight-gradient work on the side stream, or all
+    on one stream) give the oracle's bits."""
     gold = golden("c0")
-    _, recs = run_gpu("c0", I.make_config("c0"), 4)
+    _, recs = run_gpu("c0", I.make_config("c0"), 4, overlap=overlap)
     compare(recs, gold["steps"])
 
 
@@ -109,9 +113,10 @@ def test_c2_resume_across_processes(tmp_path):
     compare(second, gold["steps"][64:])
 
 
-def test_c3_three_steps_bit_exact():
+@pytest.mark.parametrize("overlap", [True, False])
+def test_c3_three_steps_bit_exact(overlap):
     gold = golden("c3")
-    _, recs = run_gpu("c3", I.make_config("c3"), 3)
+    _, recs = run_gpu("c3", I.make_config("c3"), 3, overlap=overlap)
     compare(recs, gold["steps"])
 
 
