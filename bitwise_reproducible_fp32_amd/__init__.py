@@ -63,6 +63,8 @@ _SIGS = {
     "mlb_read_stage": (i32, [vp, i32, i32, vp, sz, C.POINTER(sz)]),
     "mlb_step": (C.c_uint64, [vp]),
     "mlb_set_overlap": (i32, [vp, i32]),
+    "mlb_stage_card": (i32, [vp, i32, i32, vp]),
+    "mlb_state_card": (i32, [vp, i32, vp]),
     "mlb_stats_enable": (i32, [vp, i32]),
     "mlb_stats_read": (i32, [vp, C.POINTER(Stat), i32, C.POINTER(i32)]),
     "mlb_destroy": (i32, [vp]),
@@ -125,6 +127,11 @@ def _stream(stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+class CardStruct(C.Structure):
+    _fields_ = [("tag", C.c_char * 32), ("dtype", C.c_char * 8), ("count", C.c_uint64),
+                ("sha256", C.c_uint8 * 32)]
 
 
 class Model:
@@ -202,6 +209,29 @@ class Model:
     @property
     def step(self) -> int:
         return int(lib().mlb_step(self.h))
+
+    def _card(self, c: "CardStruct"):
+        from .cards import Card
+        return Card(c.tag.decode(), c.dtype.decode(), int(c.count), bytes(c.sha256).hex())
+
+    def stage_card(self, stage: int, layer: int = 0):
+        c = CardStruct()
+        check(lib().mlb_stage_card(self.h, stage, layer, C.byref(c)))
+        return self._card(c)
+
+    def state_card(self, which: int):
+        c = CardStruct()
+        check(lib().mlb_state_card(self.h, which, C.byref(c)))
+        return self._card(c)
+
+    def cards(self, state: bool = True) -> list:
+        """Identity cards of every stage of the last forward (computation order),
+        then of the state arrays."""
+        from .cards import card_order
+        out = [self.stage_card(st, l) for st, l in card_order(self.cfg["n_layers"])]
+        if state:
+            out += [self.state_card(w) for w in (PARAMS, GRAD, ADAM_M, ADAM_V)]
+        return out
 
     def set_overlap(self, on: bool) -> None:
         """Backward weight-gradient work on the library's second stream (default on)."""

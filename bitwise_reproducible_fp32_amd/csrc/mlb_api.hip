@@ -1027,11 +1027,47 @@ mlb_status mlb_read_stage(const mlb_model* M, int stage, int layer, void* dst, s
         float* o = static_cast<float*>(dst);
         for (int64_t z = 0; z < s.B * s.H; ++z)
             for (int64_t i = 0; i < s.T; ++i)
-                for (int64_t j = 0; j < s.T; ++j)
-                    o[(z * s.T + i) * s.T + j] = tmp[(size_t)(z * s.T * s.T + mlb::blk_index(s.T, i, j))];
+                for (int64_t j = 0; j < s.T; ++j)   // +0 above the diagonal (never part of P)
+                    o[(z * s.T + i) * s.T + j] =
+                        j <= i ? tmp[(size_t)(z * s.T * s.T + mlb::blk_index(s.T, i, j))] : 0.0f;
     } else {
         HIPCHK(hipMemcpy(dst, src, (size_t)n * 4, hipMemcpyDeviceToHost));
     }
+    return MLB_OK;
+}
+
+mlb_status mlb_stage_card(const mlb_model* M, int stage, int layer, mlb_card* out) {
+    static const char* const names[14] = {"h_in", "xn1", "r1", "qkv", "P", "O", "h_mid",
+                                          "xn2", "r2", "gu", "a", "h_L", "dlogits", "loss_rows"};
+    if (!M || !out) return fail(MLB_E_INVALID_ARG, "null argument");
+    if (stage < 0 || stage > 13) return fail(MLB_E_INVALID_ARG, "unknown stage %d", stage);
+    size_t n = 0;
+    mlb_status rc = mlb_read_stage(M, stage, layer, nullptr, 0, &n);
+    if (rc != MLB_OK) return rc;
+    std::vector<float> host(n);
+    rc = mlb_read_stage(M, stage, layer, host.data(), n * 4, &n);
+    if (rc != MLB_OK) return rc;
+    std::memset(out, 0, sizeof *out);
+    if (stage <= 10) std::snprintf(out->tag, sizeof out->tag, "L%d.%s", layer, names[stage]);
+    else std::snprintf(out->tag, sizeof out->tag, "%s", names[stage]);
+    std::snprintf(out->dtype, sizeof out->dtype, "f32");
+    out->count = n;
+    sha256_bytes(host.data(), n * 4, out->sha256);
+    return MLB_OK;
+}
+
+mlb_status mlb_state_card(const mlb_model* M, mlb_which which, mlb_card* out) {
+    static const char* const names[4] = {"params", "grad", "adam_m", "adam_v"};
+    if (!M || !out) return fail(MLB_E_INVALID_ARG, "null argument");
+    if (which < MLB_PARAMS || which > MLB_ADAM_V) return fail(MLB_E_INVALID_ARG, "unknown state array");
+    std::vector<float> host((size_t)M->s.P);
+    const mlb_status rc = mlb_read(M, which, host.data(), host.size() * 4);
+    if (rc != MLB_OK) return rc;
+    std::memset(out, 0, sizeof *out);
+    std::snprintf(out->tag, sizeof out->tag, "%s", names[which]);
+    std::snprintf(out->dtype, sizeof out->dtype, "f32");
+    out->count = (uint64_t)M->s.P;
+    sha256_bytes(host.data(), host.size() * 4, out->sha256);
     return MLB_OK;
 }
 

@@ -119,8 +119,26 @@ mlb_status mlb_read(const mlb_model* m, mlb_which which, void* host_dst, size_t 
  * input, 1 attention-norm output, 2 its 1/rms, 3 q|k|v after rotation, 4 P,
  * 5 attention output, 6 mid-layer residual, 7 MLP-norm output, 8 its 1/rms,
  * 9 g|u, 10 SwiGLU output, 11 final hidden, 12 d-logits, 13 per-row losses).
- * *count receives the element count; host_dst may be NULL to query it. */
+ * Layouts are row-major; P is dense [batch*heads, T, T] with +0 above the
+ * diagonal; d-logits are [tokens, vocab]. *count receives the element count;
+ * host_dst may be NULL to query it. */
 mlb_status mlb_read_stage(const mlb_model* m, int stage, int layer, void* host_dst, size_t bytes, size_t* count);
+
+/* Stage identity card (mojolearn PyPI page, "What bitwise identity means":
+ * per-stage hashes as a check of the identity claim): a tag ("L<layer>.<name>" for
+ * per-layer stages, else the name), the dtype and element count, and the
+ * SHA-256 of the exact bytes mlb_read_stage returns (little-endian float32).
+ * Two runs agree on a stage exactly when their cards agree, so comparing cards
+ * in computation order names the first stage where two runs diverge. */
+typedef struct mlb_card {
+    char tag[32];
+    char dtype[8];
+    uint64_t count;
+    uint8_t sha256[32];
+} mlb_card;
+mlb_status mlb_stage_card(const mlb_model* m, int stage, int layer, mlb_card* out);
+/* Card of a state array (params, accumulated gradient, AdamW moments). */
+mlb_status mlb_state_card(const mlb_model* m, mlb_which which, mlb_card* out);
 
 /* Stream overlap of the backward pass (default on). When on, the work that
  * only feeds the gradient accumulator (weight-gradient contractions, norm-gain

@@ -329,6 +329,21 @@ class Model:
         if rc != 0:
             raise ValueError(f"load refused ({rc})")
 
+    def cards(self, state: bool = True) -> list:
+        """Identity cards of the oracle's stages and state arrays, in the same
+        order and byte layout as the library's (hashed with the oracle's own
+        SHA-256)."""
+        from bitwise_reproducible_fp32_amd.cards import Card, STATE_NAMES, card_order, stage_tag
+        out = []
+        for st, l in card_order(self.cfg["n_layers"]):
+            a = self.stage(st, l)
+            out.append(Card(stage_tag(st, l), "f32", int(a.size), sha256(np.ascontiguousarray(a).tobytes())))
+        if state:
+            for w, name in enumerate(STATE_NAMES):   # params, grad, adam_m, adam_v
+                a = self.read(w)
+                out.append(Card(name, "f32", int(a.size), sha256(a.tobytes())))
+        return out
+
     def stage(self, stage: int, layer: int = 0) -> np.ndarray:
         n = lib().orc_model_stage(self.h, stage, layer, None)
         out = np.empty(n, np.float32)

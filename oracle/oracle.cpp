@@ -1006,6 +1006,12 @@ int64_t orc_model_stage(void* mp, int stage, int layer, float* dst) {
         default: return -1;
     }
     if (dst) std::memcpy(dst, s->data(), s->size() * 4);
+    if (dst && stage == 4) {   // canonical export: +0 above the diagonal (those entries are not part of P)
+        const int64_t T = M.c.seq_len, nz = (int64_t)s->size() / (T * T);
+        for (int64_t z = 0; z < nz; ++z)
+            for (int64_t i = 0; i < T; ++i)
+                for (int64_t j = i + 1; j < T; ++j) dst[(z * T + i) * T + j] = 0.0f;
+    }
     return (int64_t)s->size();
 }
 

@@ -157,6 +157,7 @@ int64_t orc_model_step(void* m);
 int64_t orc_model_save(void* m, uint8_t* buf, int64_t cap);
 int orc_model_load(void* m, const uint8_t* buf, int64_t len);
 /* Activation export of the last forward (stage id, layer); returns element count. */
+/* Stage 4 (P) is exported dense with +0 above the diagonal. */
 int64_t orc_model_stage(void* m, int stage, int layer, float* dst);
 
 #ifdef __cplusplus

@@ -137,3 +137,27 @@ def test_seeded_init_matches_oracle(name):
         assert g.save() == h.save()
         h.close()
     g.close()
+
+
+def test_stage_cards_match_oracle():
+    """Every stage and state card of the library equals the oracle's after a
+    forward and backward, and again after the AdamW step (first-divergence diff
+    reports nothing)."""
+    import bitwise_reproducible_fp32_amd as mlb
+    from bitwise_reproducible_fp32_amd.cards import first_divergence
+    cfg = I.make_config("c0")
+    init = I.init_params(cfg)
+    g, o = mlb.Model(cfg, init), oracle.Model(cfg, init)
+    x, y = I.c0_batch(0, cfg["batch"], cfg["seq_len"])
+    g.forward_loss(dev(x.astype(np.int32)), dev(y.astype(np.int32)))
+    g.backward()
+    o.forward(x, y)
+    o.backward()
+    gc, oc = g.cards(), o.cards()
+    assert len(gc) == 2 * 11 + 3 + 4
+    assert first_divergence(gc, oc) is None, first_divergence(gc, oc)
+    lr = I.lr_at("c0", 1)
+    g.adamw_step(lr)
+    o.adamw(lr)
+    assert first_divergence(g.cards(), o.cards()) is None
+    g.close()
