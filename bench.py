@@ -187,6 +187,19 @@ def main() -> int:
     elapsed = time.perf_counter() - t0
     stats = model.stats()
     model.stats_enable(False)
+
+    # inference surface (not part of the training metric): forward with loss
+    # and kept logits, and greedy next-token choices, on the same batches
+    inf_iters = 5
+    torch.cuda.synchronize()
+    t_inf = time.perf_counter()
+    for i in range(inf_iters):
+        model.infer(xd[0, i % S], yd[0, i % S])
+    t_inf = (time.perf_counter() - t_inf) / inf_iters
+    t_gr = time.perf_counter()
+    for i in range(inf_iters):
+        model.greedy_next(xd[0, i % S], T - 1)
+    t_gr = (time.perf_counter() - t_gr) / inf_iters
     for st in sorted(stats, key=lambda t: -t["ms"]):
         rate = (f"{st['flops'] / st['ms'] / 1e9:7.2f} TFLOP/s" if st["flops"] else
                 f"{st['bytes'] / st['ms'] / 1e6:7.1f} GB/s")
@@ -245,6 +258,10 @@ def main() -> int:
         "hbm_kernels": {k: {"GB/s": round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1), "ms": round(v["ms"], 3)}
                         for k, v in sorted(mem_sites.items(), key=lambda kv: -kv[1]["ms"])[:8]},
         "loss_first_last": [losses[0], losses[-1]],
+        "inference": {"tokens_per_s": round(B * T / t_inf, 1), "ms_per_batch": round(t_inf * 1e3, 2),
+                      "greedy_next_ms": round(t_gr * 1e3, 2),
+                      "what": f"forward + loss of one {B}x{T} batch with logits kept; greedy next token of {B} "
+                              f"sequences at position {T - 1} (a full forward each)"},
     }
     if not a.no_cpu_baseline:
         try:

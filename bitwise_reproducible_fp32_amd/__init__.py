@@ -63,6 +63,8 @@ _SIGS = {
     "mlb_read_stage": (i32, [vp, i32, i32, vp, sz, C.POINTER(sz)]),
     "mlb_step": (C.c_uint64, [vp]),
     "mlb_set_overlap": (i32, [vp, i32]),
+    "mlb_infer": (i32, [vp, vp, vp, vp, C.POINTER(f32)]),
+    "mlb_greedy_next": (i32, [vp, vp, i32, vp]),
     "mlb_stage_card": (i32, [vp, i32, i32, vp]),
     "mlb_state_card": (i32, [vp, i32, vp]),
     "mlb_stats_enable": (i32, [vp, i32]),
@@ -231,6 +233,21 @@ class Model:
         out = [self.stage_card(st, l) for st, l in card_order(self.cfg["n_layers"])]
         if state:
             out += [self.state_card(w) for w in (PARAMS, GRAD, ADAM_M, ADAM_V)]
+        return out
+
+    def infer(self, inputs, targets=None, logits=None):
+        """Inference forward on device int32 ids; optional device logits
+        [tokens, vocab] to fill; returns the mean loss when targets are given."""
+        loss = f32()
+        check(lib().mlb_infer(self.h, _ptr(inputs), None if targets is None else _ptr(targets),
+                              None if logits is None else _ptr(logits),
+                              None if targets is None else C.byref(loss)))
+        return None if targets is None else np.float32(loss.value)
+
+    def greedy_next(self, inputs, position: int) -> np.ndarray:
+        """Next token of every sequence after `position` (lowest index on ties)."""
+        out = np.empty(self.cfg["batch"], np.int32)
+        check(lib().mlb_greedy_next(self.h, _ptr(inputs), int(position), out.ctypes.data))
         return out
 
     def set_overlap(self, on: bool) -> None:

@@ -540,7 +540,9 @@ mlb::GemmDesc head_gemm(const Sizes& s) {
     return g;
 }
 
-mlb_status forward(mlb_model* M) {
+// mode 0: training (loss, d-logits in place of the logits); 1: inference with
+// loss (the logits are kept); 2: inference, logits only.
+mlb_status forward(mlb_model* M, int mode = 0) {
     const Sizes& s = M->s;
     hipStream_t st = M->stream;
     M->cur = st;
@@ -575,8 +577,10 @@ mlb_status forward(mlb_model* M) {
         RUN("down_fwd", wd);
     }
     RUN("head_fwd", lin(N, s.V, d, M->h[s.L], d, true, M->p + M->offOut, d, true, M->logits, s.ldV, 0));
-    OP("xent", f4 * 2 * N * s.V,
-       mlb::cross_entropy(M->logits, M->tg, N, s.V, s.ldV, M->loss_rows, M->logits, M->err, st));
+    if (mode == 2) return MLB_OK;
+    OP("xent", f4 * (mode == 0 ? 2 : 1) * N * s.V,
+       mlb::cross_entropy(M->logits, M->tg, N, s.V, s.ldV, M->loss_rows, mode == 0 ? M->logits : nullptr, M->err,
+                          st));
     OP("loss_sum", f4 * N, mlb::sum64_scaled(M->loss_rows, N, M->invN, M->loss_dev, st));
     return MLB_OK;
 }
@@ -855,6 +859,59 @@ mlb_status mlb_forward_loss(mlb_model* M, const int32_t* d_inputs, const int32_t
                          (err & 1) ? "inputs" : "targets");
     *out_loss = M->host_stage[0];
     M->have_fwd = true;
+    return MLB_OK;
+}
+
+mlb_status mlb_infer(mlb_model* M, const int32_t* d_inputs, const int32_t* d_targets, float* d_logits,
+                     float* out_loss) {
+    if (!M || !d_inputs || (d_targets && !out_loss) || (!d_targets && out_loss))
+        return fail(MLB_E_INVALID_ARG, "null argument (targets and loss go together)");
+    HIPCHK(hipSetDevice(M->device));
+    if (M->have_fwd) return fail(MLB_E_STATE, "a training forward is pending its backward");
+    const size_t nb = (size_t)M->s.N * 4;
+    HIPCHK(hipMemcpyAsync(M->ids, d_inputs, nb, hipMemcpyDeviceToDevice, M->stream));
+    if (d_targets) HIPCHK(hipMemcpyAsync(M->tg, d_targets, nb, hipMemcpyDeviceToDevice, M->stream));
+    KCHK(mlb::fill_zero(reinterpret_cast<float*>(M->err), 1, M->stream));
+    mlb_status rc = forward(M, d_targets ? 1 : 2);
+    if (rc != MLB_OK) return rc;
+    if (d_logits)
+        HIPCHK(hipMemcpy2DAsync(d_logits, (size_t)M->s.V * 4, M->logits, (size_t)M->s.ldV * 4, (size_t)M->s.V * 4,
+                                (size_t)M->s.N, hipMemcpyDeviceToDevice, M->stream));
+    HIPCHK(hipMemcpyAsync(M->host_stage, M->loss_dev, 4, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipMemcpyAsync(M->host_stage + 1, M->err, 4, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    stat_resolve(M);
+    int err;
+    std::memcpy(&err, M->host_stage + 1, 4);
+    if (err) return fail(MLB_E_BAD_TOKEN, "token id outside [0, %u) in %s", M->cfg.vocab,
+                         (err & 1) ? "inputs" : "targets");
+    if (out_loss) *out_loss = M->host_stage[0];
+    return MLB_OK;
+}
+
+mlb_status mlb_greedy_next(mlb_model* M, const int32_t* d_inputs, int position, int32_t* next_host) {
+    if (!M || !d_inputs || !next_host) return fail(MLB_E_INVALID_ARG, "null argument");
+    if (position < 0 || position >= (int)M->s.T) return fail(MLB_E_INVALID_ARG, "position %d outside the window", position);
+    HIPCHK(hipSetDevice(M->device));
+    if (M->have_fwd) return fail(MLB_E_STATE, "a training forward is pending its backward");
+    HIPCHK(hipMemcpyAsync(M->ids, d_inputs, (size_t)M->s.N * 4, hipMemcpyDeviceToDevice, M->stream));
+    KCHK(mlb::fill_zero(reinterpret_cast<float*>(M->err), 1, M->stream));
+    mlb_status rc = forward(M, 2);
+    if (rc != MLB_OK) return rc;
+    // one token per sequence: rows b * T + position of the logits; the choices
+    // land in the (unused) target buffer, then go to the host
+    M->cur = M->stream;
+    OP("argmax", 4.0 * (double)M->s.B * (double)M->s.V,
+       mlb::argmax_rows(M->logits, M->s.B, M->s.T, position, M->s.ldV, M->s.V, M->tg, M->stream));
+    HIPCHK(hipMemcpyAsync(M->host_stage + 1, M->err, 4, hipMemcpyDeviceToHost, M->stream));
+    std::vector<int32_t> host((size_t)M->s.B);
+    HIPCHK(hipMemcpyAsync(host.data(), M->tg, host.size() * 4, hipMemcpyDeviceToHost, M->stream));
+    HIPCHK(hipStreamSynchronize(M->stream));
+    stat_resolve(M);
+    int err;
+    std::memcpy(&err, M->host_stage + 1, 4);
+    if (err) return fail(MLB_E_BAD_TOKEN, "token id outside [0, %u) in inputs", M->cfg.vocab);
+    std::memcpy(next_host, host.data(), host.size() * 4);
     return MLB_OK;
 }
 

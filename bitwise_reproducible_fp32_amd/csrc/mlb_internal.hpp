@@ -113,6 +113,10 @@ int swiglu_bwd(const float* dA, const float* gu, int64_t rows, int64_t F, float*
 int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, int64_t ld, float* loss_rows,
                   float* dl, int* err, hipStream_t s);
 // out[0] = SUM64(v[0..n)) * mul.
+// out[r] = index of the largest of the first V entries of row r * row_step +
+// row_off (NaN lowest, ties to the lowest index, 0 if all NaN), r < nsel.
+int argmax_rows(const float* x, int64_t nsel, int64_t row_step, int64_t row_off, int64_t ld, int64_t V,
+                int32_t* out, hipStream_t s);
 int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s);
 // Embedding-gradient scatter. For every row v that appears in ids, in order of
 // increasing position n: acc = init(v); acc = acc + dh[n]; then

@@ -261,7 +261,8 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(const float* __restrict__ dA
 }
 
 // Cross-entropy, one wavefront per row: m = MAX64(l), Z = SUM64(exp(l - m)),
-// loss = log(Z) - (l_y - m); dl = ((exp(l - m) * (1/Z)) - [v == y]) * invN.
+// loss = log(Z) - (l_y - m); dl = ((exp(l - m) * (1/Z)) - [v == y]) * invN
+// (skipped when dl is null: inference keeps the logits).
 // A target outside [0, V) raises *err and is read as 0 (no out-of-range read).
 __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* __restrict__ tg, int64_t N,
                                               int64_t V, int64_t ld, float invN, float* __restrict__ loss_rows,
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* 
     const float Z = wave_tree_sum(acc);
     const float ly = l[y];
     if (lane == 0) loss_rows[n] = log_p(Z) - (ly - m);
+    if (!dl) return;
     const float rz = 1.0f / Z;
     float* o = dl + n * ld;
     for (int64_t v = lane; v < V; v += 64) {
@@ -290,6 +292,31 @@ __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* 
         const float t = (v == y) ? (p - 1.0f) : p;
         o[v] = t * invN;
     }
+}
+
+// Greedy choice, one wavefront per selected row r (row index r * row_step +
+// row_off of a [rows, ld] matrix): the index of the largest of the first V
+// entries; NaN ranks below every number and ties go to the lowest index (a
+// lane keeps its first maximum in ascending order, the lane tree prefers the
+// lower index on equal values); 0 when every entry is NaN.
+__global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ x, int64_t nsel, int64_t row_step,
+                                                     int64_t row_off, int64_t ld, int64_t V, int32_t* out) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (r >= nsel) return;
+    const float* row = x + (r * row_step + row_off) * ld;
+    float bv = -__builtin_inff();
+    int64_t bi = V;
+    for (int64_t v = lane; v < V; v += 64) {
+        const float t = row[v];
+        if (t > bv || (t == bv && v < bi)) { bv = t; bi = v; }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_down(bv, off);
+        const int64_t oi = __shfl_down(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) out[r] = (int32_t)(bi < V ? bi : 0);
 }
 
 // out[0] = SUM64(v) * mul, one wavefront.
@@ -524,6 +551,14 @@ int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, 
     if (N == 0) return 0;
     const float invN = 1.0f / (float)N;
     k_xent<<<blocks(N, 4), 256, 0, s>>>(logits, tg, N, V, ld, invN, loss_rows, dl, err);
+    return ok();
+}
+
+int argmax_rows(const float* x, int64_t nsel, int64_t row_step, int64_t row_off, int64_t ld, int64_t V,
+                int32_t* out, hipStream_t s) {
+    if (nsel < 0 || V <= 0 || ld < V) return -1;
+    if (nsel == 0) return 0;
+    k_argmax_rows<<<blocks(nsel, 4), 256, 0, s>>>(x, nsel, row_step, row_off, ld, V, out);
     return ok();
 }
 

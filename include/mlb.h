@@ -92,6 +92,23 @@ mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init_para
  * stream. An id outside [0, vocab) gives MLB_E_BAD_TOKEN and no usable forward. */
 mlb_status mlb_forward_loss(mlb_model* m, const int32_t* d_inputs, const int32_t* d_targets, float* out_loss_host);
 
+/* Inference forward of one batch of [batch, seq_len] device int32 ids (model
+ * card, "Using the model": forward-only logits and loss). d_logits (device,
+ * may be NULL) receives the logits [batch*seq_len, vocab] row-major; with
+ * d_targets (device, may be NULL) the mean loss goes to *out_loss_host (both
+ * or neither). The same arithmetic as the training forward: the loss equals
+ * mlb_forward_loss's bit for bit. Keeps nothing for a backward; MLB_E_STATE
+ * while a training forward awaits its backward. Synchronises the stream. */
+mlb_status mlb_infer(mlb_model* m, const int32_t* d_inputs, const int32_t* d_targets, float* d_logits,
+                     float* out_loss_host);
+/* Greedy next token of every sequence of the batch after `position`
+ * (0 <= position < seq_len): the index of the largest logit at that position,
+ * NaN ranking below every number and ties going to the lowest index (0 when
+ * every logit is NaN). Causality makes the ids after `position` irrelevant, so
+ * a prompt of p ids continues with position p - 1. next_host receives batch
+ * int32 values. Synchronises the stream. */
+mlb_status mlb_greedy_next(mlb_model* m, const int32_t* d_inputs, int position, int32_t* next_host);
+
 /* Backward of the last forward; folds its gradient g into the accumulator,
  * G = G + g (call order = micro-batch order). MLB_E_STATE without a forward. */
 mlb_status mlb_backward(mlb_model* m);

@@ -46,6 +46,12 @@ def cfg_struct(cfg: dict) -> Cfg:
                *[float(cfg[n]) for n, t in Cfg._fields_ if t is C.c_float])
 
 
+def argmax(x) -> int:
+    """Index of the largest entry: NaN below every number, ties to the lowest index."""
+    x = f32a(x).ravel()
+    return int(lib().orc_argmax(x, x.size))
+
+
 def splitmix64(seed: int, n: int) -> np.ndarray:
     """The first n SplitMix64 outputs from seed (uint64)."""
     out = np.empty(n, np.uint64)
@@ -101,6 +107,8 @@ def load(path: str = LIB_PATH):
         "orc_sha256": (None, [U8P, i64, U8P]),
         "orc_param_count": (i64, [C.POINTER(Cfg)]),
         "orc_splitmix64": (None, [C.c_uint64, i64, C.POINTER(C.c_uint64)]),
+        "orc_model_infer": (C.c_int, [C.c_void_p, I32P, C.c_void_p, C.c_void_p, C.POINTER(C.c_float)]),
+        "orc_argmax": (i64, [F32P, i64]),
         "orc_seed_params": (None, [C.POINTER(Cfg), C.c_uint64, F32P]),
         "orc_model_new": (C.c_void_p, [C.POINTER(Cfg), F32P]),
         "orc_model_free": (None, [C.c_void_p]),
@@ -328,6 +336,27 @@ class Model:
         rc = lib().orc_model_load(self.h, a, a.size)
         if rc != 0:
             raise ValueError(f"load refused ({rc})")
+
+    def infer(self, inputs, targets=None):
+        """Inference forward: (logits [tokens, vocab], mean loss or None)."""
+        x = np.ascontiguousarray(inputs, dtype=np.int32).ravel()
+        y = None if targets is None else np.ascontiguousarray(targets, dtype=np.int32).ravel()
+        N = x.size
+        logits = np.empty((N, self.cfg["vocab"]), np.float32)
+        loss = C.c_float()
+        rc = lib().orc_model_infer(self.h, x, None if y is None else y.ctypes.data, logits.ctypes.data,
+                                   C.byref(loss))
+        if rc != 0:
+            raise ValueError("token out of range")
+        return logits, (None if y is None else np.float32(loss.value))
+
+    def greedy_next(self, inputs, position: int) -> np.ndarray:
+        """Next token of each sequence after `position`: argmax of that
+        position's logits (lowest index on ties)."""
+        logits, _ = self.infer(inputs)
+        B, T = self.cfg["batch"], self.cfg["seq_len"]
+        rows = logits.reshape(B, T, -1)[:, position, :]
+        return np.array([argmax(r) for r in rows], np.int32)
 
     def cards(self, state: bool = True) -> list:
         """Identity cards of the oracle's stages and state arrays, in the same

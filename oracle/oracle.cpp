@@ -618,7 +618,9 @@ struct Model {
     float loss = 0.0f;
 };
 
-void model_forward(Model& M) {
+// keep_logits: inference; the logits stay in M.logits and the loss (when
+// targets are given) is computed into a separate d-logits buffer.
+void model_forward(Model& M, bool keep_logits = false, bool with_loss = true) {
     const orc_cfg& c = M.c;
     const int64_t N = M.N, d = c.d_model, F = c.ffn_hidden, V = c.vocab, H = c.n_heads, hd = c.head_dim;
     const int64_t B = c.batch, T = c.seq_len;
@@ -647,7 +649,12 @@ void model_forward(Model& M) {
     M.h_L = h;
     Gemm gh{N, V, d, d, h.data(), d, 1, &M.p[M.L.W_out], 1, d, 0, 1.0f, 0, 0};
     gemm_run(gh, M.logits.data(), V);
-    M.loss = cross_entropy(M.logits.data(), M.tg.data(), N, V, M.loss_rows.data(), M.logits.data());
+    if (!keep_logits) {
+        M.loss = cross_entropy(M.logits.data(), M.tg.data(), N, V, M.loss_rows.data(), M.logits.data());
+    } else if (with_loss) {
+        std::vector<float> dl_scratch(M.logits.size());
+        M.loss = cross_entropy(M.logits.data(), M.tg.data(), N, V, M.loss_rows.data(), dl_scratch.data());
+    }
 }
 
 void model_backward(Model& M) {
@@ -917,6 +924,27 @@ int orc_model_forward(void* mp, const int32_t* inputs, const int32_t* targets, f
     M.have_fwd = true;
     if (loss) *loss = M.loss;
     return 0;
+}
+
+int orc_model_infer(void* mp, const int32_t* inputs, const int32_t* targets, float* logits, float* loss) {
+    Model& M = *(Model*)mp;
+    for (int64_t i = 0; i < M.N; ++i)
+        if (inputs[i] < 0 || inputs[i] >= M.c.vocab || (targets && (targets[i] < 0 || targets[i] >= M.c.vocab)))
+            return -1;
+    M.ids.assign(inputs, inputs + M.N);
+    if (targets) M.tg.assign(targets, targets + M.N);
+    model_forward(M, true, targets != nullptr);
+    M.have_fwd = false;
+    if (logits) std::memcpy(logits, M.logits.data(), M.logits.size() * 4);
+    if (loss) *loss = targets ? M.loss : NAN;
+    return 0;
+}
+
+int64_t orc_argmax(const float* x, int64_t n) {
+    int64_t best = -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (!std::isnan(x[i]) && (best < 0 || x[i] > x[best])) best = i;
+    return best < 0 ? 0 : best;
 }
 
 int orc_model_backward(void* mp) {

@@ -146,6 +146,13 @@ void orc_model_free(void* m);
 /* Forward and loss of one micro-batch; stores activations. Returns -1 (and sets
  * *loss to NaN) on an out-of-range token. */
 int orc_model_forward(void* m, const int32_t* inputs, const int32_t* targets, float* loss);
+/* Inference forward of one batch: logits [tokens, vocab] (may be NULL) and,
+ * when targets is not NULL, the mean loss; nothing is kept for a backward.
+ * Returns -1 on an out-of-range token. */
+int orc_model_infer(void* m, const int32_t* inputs, const int32_t* targets, float* logits, float* loss);
+/* Index of the largest entry of x[0..n): NaN ranks below every number, ties go
+ * to the lowest index, 0 when every entry is NaN. */
+int64_t orc_argmax(const float* x, int64_t n);
 /* Backward of the last forward; folds its gradient into G. */
 int orc_model_backward(void* m);
 /* AdamW step with learning rate lr; G is then reset to +0. */

@@ -161,3 +161,53 @@ def test_stage_cards_match_oracle():
     o.adamw(lr)
     assert first_divergence(g.cards(), o.cards()) is None
     g.close()
+
+
+@pytest.mark.parametrize("name", ["c0", "c3"])
+def test_inference_matches_oracle(name):
+    """Inference forward: logits, loss and greedy choices equal the oracle's
+    bit for bit; the loss equals the training forward's."""
+    import torch
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config(name)
+    init = I.init_params(cfg)
+    x, y = I.batch_for(name, cfg, 1, 0)
+    xd, yd = dev(x.astype(np.int32)), dev(y.astype(np.int32))
+    g, o = mlb.Model(cfg, init), oracle.Model(cfg, init)
+    N, V, T = cfg["batch"] * cfg["seq_len"], cfg["vocab"], cfg["seq_len"]
+    logits = torch.empty(N * V, dtype=torch.float32, device="cuda")
+    loss = g.infer(xd, yd, logits)
+    ol, oloss = o.infer(x, y)
+    assert_bits(f"{name} logits", logits.cpu().numpy().reshape(N, V), ol)
+    assert np.float32(loss).tobytes() == np.float32(oloss).tobytes()
+    assert g.infer(xd) is None
+    B = cfg["batch"]
+    for pos in (0, T // 2 + 1, T - 1):
+        want = [oracle.argmax(ol.reshape(B, T, V)[b, pos]) for b in range(B)]
+        assert list(g.greedy_next(xd, pos)) == want, pos
+    train = g.forward_loss(xd, yd)
+    assert np.float32(train).tobytes() == np.float32(loss).tobytes()
+    g.backward()
+    g.close()
+
+
+def test_inference_state_rules_and_training_after_inference():
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c0")
+    m = mlb.Model(cfg, I.init_params(cfg))
+    x, y = I.batch_for("c0", cfg, 1, 0)
+    xd, yd = dev(x.astype(np.int32)), dev(y.astype(np.int32))
+    with pytest.raises(mlb.MlbError):
+        m.greedy_next(xd, cfg["seq_len"])          # position outside the window
+    m.forward_loss(xd, yd)
+    with pytest.raises(mlb.MlbError):
+        m.infer(xd)                                # a training forward awaits its backward
+    m.backward()
+    m.adamw_step(I.lr_at("c0", 1))
+    # inference in the middle of training leaves the training bits unchanged
+    m2 = mlb.Model(cfg, I.init_params(cfg))
+    m2.infer(xd, yd)
+    m2.greedy_next(xd, 5)
+    _, recs = run_gpu("c0", cfg, 1, model=m2)
+    compare(recs, golden("c0")["steps"][:1])
+    m.close()
