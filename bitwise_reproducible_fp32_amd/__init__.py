@@ -60,6 +60,7 @@ _SIGS = {
     "mlb_save": (i32, [vp, vp, sz, C.POINTER(sz)]),
     "mlb_load": (i32, [vp, vp, sz]),
     "mlb_read": (i32, [vp, i32, vp, sz]),
+    "mlb_safetensors": (i32, [C.POINTER(Config), vp, vp, sz, C.POINTER(sz)]),
     "mlb_read_stage": (i32, [vp, i32, i32, vp, sz, C.POINTER(sz)]),
     "mlb_step": (C.c_uint64, [vp]),
     "mlb_set_overlap": (i32, [vp, i32]),
@@ -119,6 +120,19 @@ def workspace_bytes(cfg: dict) -> int:
     n = sz()
     check(lib().mlb_workspace_bytes(C.byref(config(cfg)), C.byref(n)))
     return n.value
+
+
+def safetensors_bytes(cfg: dict, params: np.ndarray) -> bytes:
+    """A safetensors file image of `params` (canonical order, float32): the
+    parameter array byte for byte behind a JSON tensor table (mlb_safetensors)."""
+    p = np.ascontiguousarray(params, dtype=np.float32)
+    if p.size != param_count(cfg):
+        raise ValueError(f"{p.size} parameters, config needs {param_count(cfg)}")
+    c, n = config(cfg), sz()
+    check(lib().mlb_safetensors(C.byref(c), None, None, 0, C.byref(n)))
+    buf = np.zeros(n.value, np.uint8)
+    check(lib().mlb_safetensors(C.byref(c), p.ctypes.data, buf.ctypes.data, n.value, C.byref(n)))
+    return buf.tobytes()
 
 
 def _ptr(t) -> int:
@@ -200,6 +214,14 @@ class Model:
         out = np.empty(self.n, np.float32)
         check(lib().mlb_read(self.h, which, out.ctypes.data, out.nbytes))
         return out
+
+    def export_safetensors(self, path=None) -> bytes:
+        """The current parameters as a safetensors image (written to `path` if given)."""
+        blob = safetensors_bytes(self.cfg, self.read(PARAMS))
+        if path is not None:
+            with open(path, "wb") as f:
+                f.write(blob)
+        return blob
 
     def read_stage(self, stage: int, layer: int = 0) -> np.ndarray:
         n = sz()

@@ -19,6 +19,7 @@
 #include <map>
 #include <string>
 #include <thread>
+#include <utility>
 #include <vector>
 
 #include "../../include/mlb.h"
@@ -1031,6 +1032,60 @@ mlb_status mlb_load(mlb_model* M, const void* buf, size_t len) {
     M->step = step;
     M->n_accum = 0;
     M->have_fwd = false;
+    return MLB_OK;
+}
+
+mlb_status mlb_safetensors(const mlb_config* cfg, const float* params, void* buf, size_t cap, size_t* len) {
+    std::string why;
+    if (!len) return fail(MLB_E_INVALID_ARG, "len is null");
+    if (!cfg_valid(cfg, &why)) return fail(MLB_E_INVALID_ARG, "%s", why.c_str());
+    const Sizes s = sizes_of(cfg);
+    char num[96];
+    std::string h = "{\"__metadata__\":{\"format\":\"pt\",\"profile\":\"MLB-P1\"";
+    const std::pair<const char*, uint32_t> ints[] = {{"vocab", cfg->vocab},         {"d_model", cfg->d_model},
+                                                     {"n_layers", cfg->n_layers},   {"n_heads", cfg->n_heads},
+                                                     {"head_dim", cfg->head_dim},   {"ffn_hidden", cfg->ffn_hidden},
+                                                     {"tied", cfg->tied}};
+    for (const auto& kv : ints) {
+        std::snprintf(num, sizeof num, ",\"%s\":\"%u\"", kv.first, kv.second);
+        h += num;
+    }
+    // 9 significant digits carry a binary32 value exactly through decimal
+    std::snprintf(num, sizeof num, ",\"rope_theta\":\"%.9g\",\"rms_eps\":\"%.9g\"}", (double)cfg->rope_theta,
+                  (double)cfg->rms_eps);
+    h += num;
+    int64_t off = 0;   // byte offset in the data section; tensors in canonical order
+    auto add = [&](const std::string& name, int64_t rows, int64_t cols) {
+        const int64_t nb = rows * (cols ? cols : 1) * 4;
+        if (cols) std::snprintf(num, sizeof num, "[%lld,%lld]", (long long)rows, (long long)cols);
+        else std::snprintf(num, sizeof num, "[%lld]", (long long)rows);
+        h += ",\"" + name + "\":{\"dtype\":\"F32\",\"shape\":" + num;
+        std::snprintf(num, sizeof num, ",\"data_offsets\":[%lld,%lld]}", (long long)off, (long long)(off + nb));
+        h += num;
+        off += nb;
+    };
+    add("E_in", s.V, s.d);
+    for (int64_t l = 0; l < s.L; ++l) {
+        const std::string pre = "l" + std::to_string(l) + ".";
+        add(pre + "attn_norm", s.d, 0);
+        add(pre + "Wq", s.d, s.d); add(pre + "Wk", s.d, s.d); add(pre + "Wv", s.d, s.d); add(pre + "Wo", s.d, s.d);
+        add(pre + "mlp_norm", s.d, 0);
+        add(pre + "Wg", s.F, s.d); add(pre + "Wu", s.F, s.d); add(pre + "Wd", s.d, s.F);
+    }
+    if (!s.tied) add("W_out", s.V, s.d);
+    h += "}";
+    while (h.size() % 8) h += ' ';   // the format allows trailing spaces; keeps the data 8-byte aligned
+    if (off != s.P * 4) return fail(MLB_E_INVALID_ARG, "internal: tensor table covers %lld of %lld bytes",
+                                    (long long)off, (long long)(s.P * 4));
+    const size_t total = 8 + h.size() + (size_t)off;
+    *len = total;
+    if (!buf) return MLB_OK;
+    if (!params) return fail(MLB_E_INVALID_ARG, "params is null");
+    if (cap < total) return fail(MLB_E_IO, "buffer holds %zu bytes, %zu needed", cap, total);
+    uint8_t* b = static_cast<uint8_t*>(buf);
+    put64(b, (uint64_t)h.size());
+    std::memcpy(b + 8, h.data(), h.size());
+    std::memcpy(b + 8 + h.size(), params, (size_t)off);
     return MLB_OK;
 }
 

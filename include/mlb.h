@@ -132,6 +132,19 @@ mlb_status mlb_load(mlb_model* m, const void* host_buf, size_t len);
 /* Copies a state array (mlb_param_count floats) to host memory. */
 mlb_status mlb_read(const mlb_model* m, mlb_which which, void* host_dst, size_t bytes);
 
+/* The parameters as a safetensors file image, for running the weights in
+ * other frameworks (model card, "Anywhere else: safetensors + PyTorch": the
+ * file holds the checkpoint's parameter array byte for byte, linear weights
+ * [out_features, in_features]). Layout: u64 little-endian header length, a
+ * JSON header (padded with spaces to a multiple of 8 bytes) naming each tensor
+ * of the canonical order (E_in, l<i>.attn_norm, l<i>.Wq, Wk, Wv, Wo,
+ * l<i>.mlp_norm, l<i>.Wg, Wu, Wd, W_out) as F32 with its shape and byte range,
+ * with the shape constants under "__metadata__"; then params_host's
+ * mlb_param_count(cfg) floats unchanged. Host-only: no device is touched.
+ * buf == NULL: *len receives the size. Errors: MLB_E_INVALID_ARG (config,
+ * null params), MLB_E_IO (cap too small). */
+mlb_status mlb_safetensors(const mlb_config* cfg, const float* params_host, void* buf, size_t cap, size_t* len);
+
 /* Copies an activation of the last forward to host memory (stage ids: 0 layer
  * input, 1 attention-norm output, 2 its 1/rms, 3 q|k|v after rotation, 4 P,
  * 5 attention output, 6 mid-layer residual, 7 MLP-norm output, 8 its 1/rms,

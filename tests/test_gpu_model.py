@@ -211,3 +211,31 @@ def test_inference_state_rules_and_training_after_inference():
     _, recs = run_gpu("c0", cfg, 1, model=m2)
     compare(recs, golden("c0")["steps"][:1])
     m.close()
+
+
+def test_safetensors_export_after_training():
+    """The export of a GPU-trained model holds the checkpoint's parameter array
+    byte for byte, and the plain PyTorch forward on it agrees with the GPU's
+    inference logits to the cross-check tolerance of test_safetensors."""
+    import struct
+    import torch
+    import bitwise_reproducible_fp32_amd as mlb
+    from bitwise_reproducible_fp32_amd import torch_forward as TF
+    cfg = I.make_config("c0")
+    m, recs = run_gpu("c0", cfg, 2)
+    compare(recs, golden("c0")["steps"][:2])
+    blob = m.export_safetensors()
+    (n,) = struct.unpack("<Q", blob[:8])
+    ck = m.save()
+    nb = m.n * 4
+    hdr = len(ck) - 3 * nb
+    assert blob[8 + n:] == ck[hdr:hdr + nb]
+    x, _ = I.batch_for("c0", cfg, 3, 0)
+    N, V = cfg["batch"] * cfg["seq_len"], cfg["vocab"]
+    logits = torch.empty(N * V, dtype=torch.float32, device="cuda")
+    m.infer(dev(x.astype(np.int32)), None, logits)
+    got = logits.cpu().numpy().reshape(N, V).astype(np.float64)
+    ctx, t = TF.load(blob)
+    ref = TF.forward_logits(ctx, t, x.reshape(cfg["batch"], cfg["seq_len"])).reshape(N, V).numpy()
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+    m.close()
