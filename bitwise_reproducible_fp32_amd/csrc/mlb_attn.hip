@@ -158,7 +158,185 @@ __global__ __launch_bounds__(256) void k_tri_nt(TriArgs a) {
     store(c11, 32, 32);
 }
 
+// ----------------------------------------------------------------------------
+// Causal contractions against the attention matrix for 64-wide heads:
+//   KR 1: C[i][c] = sum over k <= i of P[i][k] B[k][c]   (O = P v, dQ = dS k)
+//   KR 2: C[j][c] = sum over k >= j of P[k][j] B[k][c]   (dV = P^T dO, dK = dS^T q)
+// P is [T, T] per head in 32x32 tiles (4 KiB contiguous, row-major inside,
+// T/32 tiles per tile row); B and C are row-major with their own strides.
+// G1024: every output is an fma chain from +0 in ascending k over each
+// 1024-chunk of k intersected with its causal range; the non-empty chunk
+// results are added left to right (here in registers: the chunk accumulator
+// is folded into a running total when k crosses a multiple of 1024).
+//
+// A workgroup (4 waves, each one 32x32 MFMA block) owns 64 output rows x 64
+// columns of two row tiles, r and T/64 - 1 - r, one after the other. Along the
+// diagonal the k range of tile r has r + 1 (KR 1) or T/64 - r (KR 2) stages
+// of 64, so every pair holds T/64 + 1 stages and all workgroups finish
+// together. Each stage stages 64x64 of P and 64x64 of B through LDS with the
+// next stage prefetched into registers (across the switch to the second tile
+// as well). The 32x32 blocks that straddle the diagonal take the MFMA pair for
+// rows that use both terms and one fma for the row that uses only one, in the
+// same ascending order. Upper-triangle parts of P that a stage loads are never
+// used.
+constexpr int AV = 64;          // rows per tile, k per stage, output columns
+constexpr int AV_BLD = AV + 4;  // LDS row of B, and of A when k-major (KR 2)
+
+struct AvArgs {
+    int64_t T, H, npairs;
+    const float* A; int64_t sAb, sAh;
+    const float* B; int64_t ldb, sBb, sBh;
+    float* C; int64_t ldc, sCb, sCh;
+};
+
+template <int KR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void k_attn_av(AvArgs a) {
+    // KR 1: A(i, k) = P[i][k], held i-major (row stride 65: the lanes of a
+    // wave read 32 rows at one k without bank conflicts). KR 2: A(j, k) =
+    // P[k][j], held k-major as loaded.
+    constexpr int ALD = KR == 1 ? AV + 1 : AV_BLD;
+    __shared__ float As[AV * ALD];
+    __shared__ float Bs[AV * AV_BLD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wc = wave >> 1;   // the wave's 32-row and 32-column block
+    const int lk = lane >> 5, li = lane & 31;
+    const int64_t lb = xcd_logical_block();   // whole heads per XCD: B stays in one L2
+    const int64_t z = lb / a.npairs, pr = lb % a.npairs;
+    const int64_t zb = z / a.H, zh = z % a.H;
+    const float* __restrict__ P = a.A + zb * a.sAb + zh * a.sAh;
+    const float* __restrict__ Bm = a.B + zb * a.sBb + zh * a.sBh;
+    float* __restrict__ C = a.C + zb * a.sCb + zh * a.sCh;
+    const int64_t nrt = a.T / AV, ptr = a.T / 32;   // row tiles; P tiles per tile row
+    const int64_t ta = pr, tb = nrt - 1 - pr;       // tb == ta: a single tile
+    auto nstages = [&](int64_t t) -> int64_t { return KR == 1 ? t + 1 : nrt - t; };
+    auto first_k = [&](int64_t t) -> int64_t { return KR == 1 ? 0 : t * AV; };
+    const int64_t na = nstages(ta), nsteps = na + (tb != ta ? nstages(tb) : 0);
+
+    // prefetch registers as scalars and helpers forced inline: an array of
+    // float4 captured by the lambdas was placed in scratch memory, which made
+    // every load wait for its data at once
+    float ra[16], rb[16];
+    auto load = [&](int64_t st) __attribute__((always_inline)) {
+        const int64_t t = st < na ? ta : tb;
+        const int64_t k0 = first_k(t) + AV * (st < na ? st : st - na), r0 = t * AV;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int q = tid + 256 * s, b = q >> 8, w = q & 255;
+            // P tile (b >> 1, b & 1) of the stage: KR 1 (rows r0.., k0..), KR 2 (rows k0.., cols r0..)
+            const int64_t pr_ = (KR == 1 ? r0 : k0) / 32 + (b >> 1), pc_ = (KR == 1 ? k0 : r0) / 32 + (b & 1);
+            const float4 va = *reinterpret_cast<const float4*>(P + ((pr_ * ptr + pc_) << 10) + w * 4);
+            const float4 vb = *reinterpret_cast<const float4*>(Bm + (k0 + (q >> 4)) * a.ldb + (q & 15) * 4);
+            ra[4 * s + 0] = va.x; ra[4 * s + 1] = va.y; ra[4 * s + 2] = va.z; ra[4 * s + 3] = va.w;
+            rb[4 * s + 0] = vb.x; rb[4 * s + 1] = vb.y; rb[4 * s + 2] = vb.z; rb[4 * s + 3] = vb.w;
+        }
+    };
+    auto store_lds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int q = tid + 256 * s, b = q >> 8, w = q & 255;
+            const int rr = 32 * (b >> 1) + (w >> 3), cc = 32 * (b & 1) + (w & 7) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                As[rr * ALD + cc + e] = ra[4 * s + e];
+                Bs[(q >> 4) * AV_BLD + (q & 15) * 4 + e] = rb[4 * s + e];
+            }
+        }
+    };
+    auto a_lds = [&](int r, int k) -> float { return KR == 1 ? As[r * ALD + k] : As[k * ALD + r]; };
+    const int rl = 32 * wr, cl = 32 * wc + li;   // wave's first local row; lane's local column
+
+    v16f acc, tot;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { acc[e] = 0.0f; tot[e] = 0.0f; }
+    bool have = false, dirty = false;
+    load(0);
+    for (int64_t st = 0; st < nsteps; ++st) {
+        const bool second = st >= na;
+        const int64_t t = second ? tb : ta, sl = second ? st - na : st;
+        const int64_t k0 = first_k(t) + AV * sl, rb0 = t * AV + rl;   // stage k, the wave's first row
+        __syncthreads();
+        store_lds();
+        __syncthreads();
+        if (st + 1 < nsteps) load(st + 1);
+        if (sl > 0 && k0 % 1024 == 0 && dirty) {   // a new chunk: fold the finished one
+#pragma unroll
+            for (int e = 0; e < 16; ++e) { tot[e] = have ? tot[e] + acc[e] : acc[e]; acc[e] = 0.0f; }
+            have = true;
+            dirty = false;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t kb0 = k0 + 32 * h;
+            const int ko = 32 * h;
+            const int stt = KR == 1 ? (kb0 < rb0 ? 1 : (kb0 == rb0 ? 2 : 0)) : (kb0 > rb0 ? 1 : (kb0 == rb0 ? 2 : 0));
+            if (stt == 1) {
+                dirty = true;
+#pragma unroll 8
+                for (int p = 0; p < 16; ++p) {
+                    const int kk = ko + 2 * p + lk;
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a_lds(rl + li, kk), Bs[kk * AV_BLD + cl], acc, 0, 0, 0);
+                }
+            } else if (stt == 2) {
+                // diagonal block: per k-pair (ka, kb) relative to the block's
+                // first row, rows that take both terms keep the pair's result,
+                // the one row whose range ends between them takes one fma
+                dirty = true;
+#pragma unroll 1
+                for (int p = 0; p < 16; ++p) {
+                    const int kk = ko + 2 * p + lk;
+                    const v16f n = __builtin_amdgcn_mfma_f32_32x32x2f32(a_lds(rl + li, kk), Bs[kk * AV_BLD + cl], acc,
+                                                                        0, 0, 0);
+                    const int ka = 2 * p, kb = 2 * p + 1;
+                    const int ks = KR == 1 ? ka : kb;   // the single term's k, also its row
+                    const float as = a_lds(rl + ks, ko + ks), bs = Bs[(ko + ks) * AV_BLD + cl];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int il = 8 * (e >> 2) + 4 * lk + (e & 3);
+                        const bool both = KR == 1 ? (il >= kb) : (il <= ka);
+                        const float s1 = __builtin_fmaf(as, bs, acc[e]);
+                        acc[e] = both ? n[e] : (il == ks ? s1 : acc[e]);
+                    }
+                }
+            }
+        }
+        const bool last = (st + 1 == nsteps) || (st + 1 == na);
+        if (last) {   // the tile's outputs: fold the last chunk, store, reset
+            float* Ct = C + (t * AV + rl) * a.ldc + 32 * wc + li;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float v = have ? (dirty ? tot[e] + acc[e] : tot[e]) : acc[e];
+                Ct[(int64_t)(8 * (e >> 2) + 4 * lk + (e & 3)) * a.ldc] = v;
+                acc[e] = 0.0f;
+                tot[e] = 0.0f;
+            }
+            have = false;
+            dirty = false;
+        }
+    }
+}
+
 }  // namespace
+
+bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
+                  int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh) {
+    if (hd != AV || T <= 0 || T % AV != 0 || ldp != T || batch < 1 || H < 1 || batch % H) return false;
+    return ((uintptr_t)P & 15u) == 0 && ((uintptr_t)B & 15u) == 0 && ldb % 4 == 0 && sBb % 4 == 0 && sBh % 4 == 0 &&
+           sPb % 4 == 0 && sPh % 4 == 0;
+}
+
+int attn_av(int kr, int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
+            int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb,
+            int64_t sCh, hipStream_t s) {
+    if (kr != 1 && kr != 2) return -1;
+    if (!attn_av_fits(T, hd, batch, H, P, ldp, sPb, sPh, B, ldb, sBb, sBh)) return -2;
+    const int64_t npairs = (T / AV + 1) / 2;
+    AvArgs a{T, H, npairs, P, sPb, sPh, B, ldb, sBb, sBh, C, ldc, sCb, sCh};
+    const dim3 grid((unsigned)(npairs * batch));
+    if (kr == 1) k_attn_av<1><<<grid, 256, 0, s>>>(a);
+    else k_attn_av<2><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
            const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,

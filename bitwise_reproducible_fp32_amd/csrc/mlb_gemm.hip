@@ -665,6 +665,18 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     a.H = d.H; a.sAb = d.sAb; a.sAh = d.sAh; a.sBb = d.sBb; a.sBh = d.sBh; a.sCb = d.sCb; a.sCh = d.sCh;
     a.outmask = d.outmask; a.mode = d.mode; a.krange = d.krange; a.scale = d.scale;
     a.split = 0; a.part = nullptr; a.chunk = -1; a.tm_lo = 0;
+    // The causal attention contractions of 64-wide heads (tiled P, square,
+    // one segment) have their own kernel when the plan leaves the choice open.
+    if (p.tile < 0 && p.split < 0 && !p.simple && d.a_blk && d.mode == 0 && !d.outmask && !d.b_kc &&
+        d.M == d.K && d.kseg == d.K && ((d.krange == 1 && d.a_kc) || (d.krange == 2 && !d.a_kc)) &&
+        attn_av_fits(d.M, d.N, d.batch, d.H, d.A, d.lda, d.sAb, d.sAh, d.B, d.ldb, d.sBb, d.sBh)) {
+        std::snprintf(g_launched, sizeof g_launched, "k_attn_av<%d>", d.krange);
+        t.begin();
+        const int r = attn_av(d.krange, d.M, d.N, d.batch, d.H, d.A, d.lda, d.sAb, d.sAh, d.B, d.ldb, d.sBb, d.sBh,
+                              d.C, d.ldc, d.sCb, d.sCh, s);
+        t.end(gemm_flops(d, 0, d.K), 0.0);
+        return r;
+    }
     if (p.simple || d.K == 0) {
         const int64_t n = d.M * d.N;
         const dim3 grid((unsigned)((n + 255) / 256), 1, (unsigned)d.batch);

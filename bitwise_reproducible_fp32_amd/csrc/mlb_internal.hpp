@@ -77,6 +77,17 @@ const char* gemm_last_kernel();
 // blk: C is stored in the tiled layout (ldc = T, a multiple of 32).
 // P and D non-null (scaled 0): softmax backward in the epilogue, C(i,j) =
 // (P(i,j) * (t(i,j) - D[z*T + i])) * ds_scale, with P laid out as C.
+// Causal contraction of 64-wide heads against the tiled attention matrix P
+// ([T, T] per head in 32x32 tiles, row length ldp == T): kr 1 C[i] = sum over
+// k <= i of P[i][k] B[k], kr 2 C[j] = sum over k >= j of P[k][j] B[k], the
+// G1024 rule, mode 0 (mlb_attn.hip). Returns -2 when the shape is not one it
+// runs (hd != 64, T not a multiple of 64, misaligned operands): the caller
+// then uses the general contraction.
+bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
+                  int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh);
+int attn_av(int kr, int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
+            int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb,
+            int64_t sCh, hipStream_t s);
 int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
            const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
            int scaled, float scale, int blk, const float* P, const float* D, float ds_scale, hipStream_t s);

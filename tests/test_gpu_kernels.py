@@ -248,8 +248,12 @@ def test_rope(mlb):
         assert_bits(f"rope bwd={bwd}", host(xd), want)
 
 
+# hd = 64 with T a multiple of 64 and tiled P runs the paired-row-tile
+# kernel (single tile, odd tile count, one and two 1024-chunks); the other
+# shapes run the general contraction.
 @pytest.mark.parametrize("BH,T,hd,tiled", [(2, 64, 8, 0), (2, 64, 8, 1), (3, 300, 5, 0), (2, 1100, 64, 0),
-                                           (2, 1088, 64, 1), (3, 96, 5, 1), (1, 2080, 64, 1)])
+                                           (2, 1088, 64, 1), (3, 96, 5, 1), (1, 2080, 64, 1), (2, 64, 64, 1),
+                                           (3, 192, 64, 1), (2, 1024, 64, 1), (1, 2048, 64, 1)])
 def test_attention_fwd_bwd(mlb, BH, T, hd, tiled):
     rng = np.random.default_rng(T + hd)
     q, k, v, dO = (make(rng, (BH, T, hd)) for _ in range(4))
@@ -269,6 +273,37 @@ def test_attention_fwd_bwd(mlb, BH, T, hd, tiled):
     assert_bits("dq", host(dq).reshape(BH, T, hd), dqo)
     assert_bits("dk", host(dk).reshape(BH, T, hd), dko)
     assert_bits("dv", host(dv).reshape(BH, T, hd), dvo)
+
+
+def test_attention_strided_heads(mlb):
+    """Heads as column slices of [B*T, 3*H*hd] (the step's layout), output
+    rows of stride H*hd, every contraction routed through the paired-row-tile
+    kernel; each head equals the oracle's."""
+    B, H, T, hd = 2, 3, 1152, 64
+    rng = np.random.default_rng(77)
+    qkv = make(rng, (B * T, 3 * H * hd))
+    dO = make(rng, (B * T, H * hd))
+    ld, ldo = 3 * H * hd, H * hd
+    qkvd = dev(qkv).reshape(-1)
+    q, k, v = qkvd, qkvd[H * hd:], qkvd[2 * H * hd:]      # column offsets of the flat buffer
+    P, O = empty(B * H * T * T), empty(B * T * ldo)
+    mlb.attention_fwd(B, H, T, hd, q, k, v, ld, P, O, ldo, tiled=1)
+    dqkv = empty(B * T * ld)
+    dqkv.zero_()
+    ws = empty(B * H * T * T + B * H * T)
+    mlb.attention_bwd(B, H, T, hd, q, k, v, ld, P, O, dev(dO), ldo, dqkv, dqkv[H * hd:], dqkv[2 * H * hd:], ws,
+                      tiled=1)
+    Og, dg = host(O).reshape(B, T, H, hd), host(dqkv).reshape(B, T, 3, H, hd)
+    for b in range(B):
+        for h in range(H):
+            x = qkv.reshape(B, T, 3, H, hd)[b, :, :, h]
+            qh, kh, vh = (np.ascontiguousarray(x[:, i])[None] for i in range(3))
+            Po, Oo = oracle.attention_fwd(qh, kh, vh)
+            assert_bits(f"O b{b} h{h}", Og[b, :, h], Oo[0])
+            dOh = np.ascontiguousarray(dO.reshape(B, T, H, hd)[b, :, h])[None]
+            want = oracle.attention_bwd(qh, kh, vh, Po, Oo, dOh)
+            for i, name in enumerate(("dq", "dk", "dv")):
+                assert_bits(f"{name} b{b} h{h}", dg[b, :, i, h], want[i][0])
 
 
 def test_swiglu(mlb):
