@@ -527,6 +527,26 @@ mlb_status run_tri(mlb_model* M, const char* site, int64_t T, int64_t hd, const 
     return MLB_OK;
 }
 
+// The row-strip kernel for 64-wide heads: the scores (P == nullptr), or dS
+// together with dQ. Returns MLB_E_UNSUPPORTED without launching when the
+// shape is not one it runs.
+mlb_status run_rows(mlb_model* M, const char* site, const float* X, int64_t ldx, const float* Y, int64_t ldy,
+                    float* S, float scale, const float* P = nullptr, const float* D = nullptr,
+                    const float* K = nullptr, int64_t ldk = 0, float* dQ = nullptr, int64_t ldq = 0) {
+    const Sizes& s = M->s;
+    const int64_t T = s.T, hd = s.hd;
+    if (!mlb::attn_rows_fits(T, hd, s.B * s.H, s.H, X, ldx, T * ldx, hd, Y, ldy, T * ldy, hd, S, T, s.H * T * T,
+                             T * T))
+        return MLB_E_UNSUPPORTED;
+    const double tri = 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd;
+    const int64_t ev = stat_begin(M);
+    const int r = mlb::attn_rows(T, hd, s.B * s.H, s.H, X, ldx, T * ldx, hd, Y, ldy, T * ldy, hd, S, T, s.H * T * T,
+                                 T * T, scale, P, D, K, ldk, T * ldk, hd, dQ, ldq, T * ldq, hd, M->cur);
+    stat_end(M, ev, site, P ? "k_attn_rows<dS,dQ>" : "k_attn_rows<S>", P ? 2.0 * tri : tri, 0.0);
+    if (r != 0) return fail(MLB_E_DEVICE, "%s failed (%d)", site, r);
+    return MLB_OK;
+}
+
 #define TRI(site, ...)                                       \
     do {                                                     \
         mlb_status st_ = run_tri(M, site, __VA_ARGS__);      \
@@ -557,8 +577,12 @@ mlb_status forward(mlb_model* M, int mode = 0) {
         OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
         OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
         // S = (q . k) * scale, j <= i
-        TRI("attn_scores", T, hd, M->qkv[l], 3 * d, T * 3 * d, M->qkv[l] + d, 3 * d, T * 3 * d, M->P[l], 1,
-            M->attn_scale);
+        const mlb_status sr = run_rows(M, "attn_scores", M->qkv[l], 3 * d, M->qkv[l] + d, 3 * d, M->P[l],
+                                       M->attn_scale);
+        if (sr == MLB_E_UNSUPPORTED)
+            TRI("attn_scores", T, hd, M->qkv[l], 3 * d, T * 3 * d, M->qkv[l] + d, 3 * d, T * 3 * d, M->P[l], 1,
+                M->attn_scale);
+        else if (sr != MLB_OK) return sr;
         OP("softmax_fwd", f4 * 2 * tri, mlb::softmax_causal(M->P[l], BH, T, 1, st));
         mlb::GemmDesc pv = head_gemm(s);   // O = P v over j <= i
         pv.M = T; pv.N = hd; pv.K = T; pv.kseg = T; pv.a_blk = true; pv.krange = 1;
@@ -684,11 +708,16 @@ mlb_status backward(mlb_model* M) {
         CHK(ring_read(M, DH, kh1));
         on_main();
         OP("attn_rowdot", f4 * (2 * N * d + BH * T), mlb::attn_rowdot(M->dO, M->O[l], s.B, H, T, hd, d, M->Dv, st));
-        // dS = (P * (dO . v - D)) * scale, j <= i (dP never reaches memory)
-        TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f, M->P[l], M->Dv,
-            M->attn_scale);
         CHK(ring_claim(M, DQKV, kq));
         float* dqkv = DQKV.buf[kq];
+        // dS = (P * (dO . v - D)) * scale, j <= i (dP never reaches memory);
+        // with 64-wide heads dQ = dS k in the same pass
+        const mlb_status dr = run_rows(M, "attn_ds_dq", M->dO, d, M->qkv[l] + 2 * d, 3 * d, M->dP, M->attn_scale,
+                                       M->P[l], M->Dv, M->qkv[l] + d, 3 * d, dqkv, 3 * d);
+        if (dr == MLB_E_UNSUPPORTED)
+            TRI("attn_dp", T, hd, M->dO, d, T * d, M->qkv[l] + 2 * d, 3 * d, T * 3 * d, M->dP, 0, 1.0f, M->P[l],
+                M->Dv, M->attn_scale);
+        else if (dr != MLB_OK) return dr;
         mlb::GemmDesc dv = head_gemm(s);   // dv = P^T dO over i >= j
         dv.M = T; dv.N = hd; dv.K = T; dv.kseg = T; dv.a_blk = true; dv.krange = 2;
         dv.A = M->P[l]; dv.lda = T; dv.a_kc = false; dv.sAb = H * T * T; dv.sAh = T * T;
@@ -700,7 +729,7 @@ mlb_status backward(mlb_model* M) {
         dq.A = M->dP; dq.lda = T; dq.a_kc = true; dq.sAb = H * T * T; dq.sAh = T * T;
         dq.B = M->qkv[l] + d; dq.ldb = 3 * d; dq.b_kc = false; dq.sBb = T * 3 * d; dq.sBh = hd;
         dq.C = dqkv; dq.ldc = 3 * d; dq.sCb = T * 3 * d; dq.sCh = hd;
-        RUN("attn_dq", dq);
+        if (dr == MLB_E_UNSUPPORTED) RUN("attn_dq", dq);
         mlb::GemmDesc dk = head_gemm(s);   // dk = dS^T q over i >= j
         dk.M = T; dk.N = hd; dk.K = T; dk.kseg = T; dk.a_blk = true; dk.krange = 2;
         dk.A = M->dP; dk.lda = T; dk.a_kc = false; dk.sAb = H * T * T; dk.sAh = T * T;
@@ -1325,7 +1354,13 @@ mlb_status mlb_prim_attention_fwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     hipStream_t st = static_cast<hipStream_t>(stream);
     mlb::GemmPlan plan;
     const float scale = (float)(1.0 / std::sqrt((double)hd));
-    if (hd <= 64) {
+    const bool rows = p_tiled && mlb::attn_rows_fits(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T,
+                                                     H * T * T, T * T);
+    if (rows) {
+        if (mlb::attn_rows(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T, H * T * T, T * T, scale,
+                           nullptr, nullptr, nullptr, 0, 0, 0, nullptr, 0, 0, 0, st))
+            return fail(MLB_E_DEVICE, "scores");
+    } else if (hd <= 64) {
         if (mlb::tri_nt(T, hd, B * H, H, q, ld, T * ld, hd, k, ld, T * ld, hd, P, T, H * T * T, T * T, 1, scale,
                         p_tiled, nullptr, nullptr, 0.0f, st))
             return fail(MLB_E_DEVICE, "scores");
@@ -1365,7 +1400,15 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     mlb::GemmPlan plan;
     const float scale = (float)(1.0 / std::sqrt((double)hd));
     if (mlb::attn_rowdot(dO, O, B, H, T, hd, ldo, D, st)) return fail(MLB_E_DEVICE, "rowdot");
-    if (hd <= 64) {
+    const bool rows = p_tiled && mlb::attn_rows_fits(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T,
+                                                     H * T * T, T * T) &&
+                      ((uintptr_t)k & 15u) == 0 && ld % 4 == 0;
+    if (rows) {
+        // dS and dQ in one pass
+        if (mlb::attn_rows(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T, H * T * T, T * T, scale, P,
+                           D, k, ld, T * ld, hd, dq, ld, T * ld, hd, st))
+            return fail(MLB_E_DEVICE, "dS");
+    } else if (hd <= 64) {
         // dS directly: the softmax backward runs in the epilogue
         if (mlb::tri_nt(T, hd, B * H, H, dO, ldo, T * ldo, hd, v, ld, T * ld, hd, dP, T, H * T * T, T * T, 0, 1.0f,
                         p_tiled, P, D, scale, st))
@@ -1393,7 +1436,7 @@ mlb_status mlb_prim_attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, c
     gq.A = dP; gq.lda = T; gq.a_kc = true; gq.sAb = H * T * T; gq.sAh = T * T;
     gq.B = k; gq.ldb = ld; gq.b_kc = false; gq.sBb = T * ld; gq.sBh = hd;
     gq.C = dq; gq.ldc = ld; gq.sCb = T * ld; gq.sCh = hd;
-    if (mlb::gemm(gq, plan, st)) return fail(MLB_E_DEVICE, "dq");
+    if (!rows && mlb::gemm(gq, plan, st)) return fail(MLB_E_DEVICE, "dq");
     mlb::GemmDesc gk;
     gk.batch = B * H; gk.H = H;
     gk.M = T; gk.N = hd; gk.K = T; gk.kseg = T; gk.krange = 2; gk.a_blk = p_tiled != 0;

@@ -316,7 +316,249 @@ void k_attn_av(AvArgs a) {
     }
 }
 
+// ----------------------------------------------------------------------------
+// Row-strip kernels over the lower triangle for 64-wide heads. A workgroup
+// owns two 64-row tiles (r and T/64 - 1 - r, so every workgroup has T/64 + 1
+// steps) and walks each one's column tiles j0 = 0, 64, .., i0 in ascending
+// order. Per step, each wave computes one 32x32 block of X Y^T over the 64
+// head positions (an fma chain from +0 in ascending h, the rule for a single
+// chunk) with the strip's X rows held in LDS for the whole row tile and the
+// Y tile staged per step, the next one prefetched into registers.
+//   scores (DS false): S = t * scale for j <= i, stored in the tiled layout.
+//   DS true: t = dO . v (dP), dS = (P * (t - D_i)) * scale, stored tiled; and
+//   in the same walk dQ_i = sum over j <= i of dS_ij k_j, whose ascending j
+//   order is exactly its G1024 chain (chunks of 1024 folded in registers), so
+//   dS is not read back for dQ. The diagonal block of dQ takes the MFMA pair
+//   for rows that use both terms and one fma for the row that uses one.
+struct RowsArgs {
+    int64_t T, H, npairs;
+    const float* X; int64_t ldx, sXb, sXh;   // q (scores) or dO (dS): rows i
+    const float* Y; int64_t ldy, sYb, sYh;   // k (scores) or v (dS): rows j
+    float* S; int64_t sSb, sSh;              // tiled [T, T] output
+    float scale;
+    const float* P;                          // dS: tiled P, strides of S
+    const float* D;                          // dS: [batch][T]
+    const float* K; int64_t ldk, sKb, sKh;   // dS: k rows (dQ's right operand)
+    float* dQ; int64_t ldq, sQb, sQh;        // dS: dQ rows
+};
+
+template <bool DS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void k_attn_rows(RowsArgs a) {
+    constexpr int LR = AV + 1;   // odd LDS row: 32 lanes reading 32 rows at one column hit 32 banks
+    __shared__ float Xs[AV * LR];             // strip rows [i][h]
+    __shared__ float Ys[AV * LR];             // Y tile [j][h], then (dS) the k tile [j][h]
+    __shared__ float Ss[DS ? AV * LR : 1];    // dS tile [i][j] for the dQ contraction
+    __shared__ float Dv[DS ? AV : 1];         // D of the strip's rows
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave & 1, wc = wave >> 1;
+    const int lk = lane >> 5, li = lane & 31;
+    const int64_t lb = xcd_logical_block();
+    const int64_t z = lb / a.npairs, pr = lb % a.npairs;
+    const int64_t zb = z / a.H, zh = z % a.H;
+    const float* __restrict__ X = a.X + zb * a.sXb + zh * a.sXh;
+    const float* __restrict__ Y = a.Y + zb * a.sYb + zh * a.sYh;
+    float* __restrict__ S = a.S + zb * a.sSb + zh * a.sSh;
+    const float* __restrict__ Pz = DS ? a.P + zb * a.sSb + zh * a.sSh : nullptr;
+    const float* __restrict__ Dz = DS ? a.D + z * a.T : nullptr;
+    const float* __restrict__ Kz = DS ? a.K + zb * a.sKb + zh * a.sKh : nullptr;
+    float* __restrict__ Q = DS ? a.dQ + zb * a.sQb + zh * a.sQh : nullptr;
+    const int64_t nrt = a.T / AV, ptr = a.T / 32;
+    const int64_t ta = pr, tb = nrt - 1 - pr;
+    const int64_t na = ta + 1, nsteps = na + (tb != ta ? tb + 1 : 0);
+
+    // prefetch registers (scalars, helpers inline: see k_attn_av)
+    float rx[16], ry[16], rk[16];
+    // Addresses are a workgroup-uniform base plus an unsigned 32-bit lane
+    // offset (every per-head offset is below 2^32 / 4): one VGPR per address.
+    auto load_rows = [&](const float* base, uint32_t ld, uint32_t r0, float* dst) __attribute__((always_inline)) {
+        const uint32_t o = (r0 + (uint32_t)(tid >> 4)) * ld + (uint32_t)(tid & 15) * 4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float4 v = *reinterpret_cast<const float4*>(base + (o + 16u * (uint32_t)s * ld));
+            dst[4 * s + 0] = v.x; dst[4 * s + 1] = v.y; dst[4 * s + 2] = v.z; dst[4 * s + 3] = v.w;
+        }
+    };
+    auto put_rows = [&](float* dst, const float* src) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int q = tid + 256 * s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(q >> 4) * LR + (q & 15) * 4 + e] = src[4 * s + e];
+        }
+    };
+    auto tile_of = [&](int64_t st, int64_t& t, int64_t& sl) __attribute__((always_inline)) {
+        const bool second = st >= na;
+        t = second ? tb : ta;
+        sl = second ? st - na : st;
+    };
+    // operands of step st: the strip rows (first step of a row tile) and the
+    // Y tile; the k tile separately, later (it is used only after the dP part)
+    auto prefetch_y = [&](int64_t st) __attribute__((always_inline)) {
+        int64_t t, sl;
+        tile_of(st, t, sl);
+        if (sl == 0) load_rows(X, (uint32_t)a.ldx, (uint32_t)(t * AV), rx);
+        load_rows(Y, (uint32_t)a.ldy, (uint32_t)(sl * AV), ry);
+    };
+    auto prefetch_k = [&](int64_t st) __attribute__((always_inline)) {
+        int64_t t, sl;
+        tile_of(st, t, sl);
+        load_rows(Kz, (uint32_t)a.ldk, (uint32_t)(sl * AV), rk);
+    };
+
+    v16f qacc, qtot;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { qacc[e] = 0.0f; qtot[e] = 0.0f; }
+    bool have = false, dirty = false;
+    const int rl = 32 * wr;                   // the wave's first row in the strip
+    auto row_of = [&](int e) -> int { return 8 * (e >> 2) + 4 * lk + (e & 3); };   // MFMA output row of element e
+    prefetch_y(0);
+    if (DS) prefetch_k(0);
+    for (int64_t st = 0; st < nsteps; ++st) {
+        int64_t t, sl;
+        tile_of(st, t, sl);
+        const int64_t i0 = t * AV, j0 = sl * AV;
+        const bool diag_tile = sl == t;
+        __syncthreads();                      // readers of the previous step's LDS are done
+        if (sl == 0) {
+            put_rows(Xs, rx);
+            if (DS && tid < AV) Dv[tid] = Dz[i0 + tid];
+        }
+        put_rows(Ys, ry);
+        __syncthreads();
+        // this wave's block: rows i0 + rl, columns j0 + 32 wc; above the diagonal: nothing
+        const bool active = !(diag_tile && wc > wr);
+        // this wave's 32x32 block of the tiled [T, T] layouts, and the lane's column in it
+        const uint32_t blk = ((uint32_t)((i0 + rl) >> 5) * (uint32_t)ptr + (uint32_t)((j0 >> 5) + wc)) << 10;
+        float pv[16];
+        if (DS && active) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) pv[e] = Pz[blk + (uint32_t)(row_of(e) * 32 + li)];
+        }
+        v16f acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+        if (active) {
+#pragma unroll 8
+            for (int p = 0; p < 32; ++p) {
+                const int h = 2 * p + lk;
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(Xs[(rl + li) * LR + h], Ys[(32 * wc + li) * LR + h], acc, 0,
+                                                           0, 0);
+            }
+        }
+        v16f& x = acc;   // the stored values, in place
+        if (DS) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = (pv[e] * (acc[e] - Dv[rl + row_of(e)])) * a.scale;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[e] = acc[e] * a.scale;
+        }
+        if (active) {
+            // The tiled block is contiguous (row r at r * 32). The diagonal
+            // block is stored whole: its part above the diagonal is never
+            // read as a value (the softmax and every contraction take j <= i
+            // only, and the exported P shows +0 there).
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S[blk + (uint32_t)(row_of(e) * 32 + li)] = x[e];
+        }
+        if (DS) {
+            __syncthreads();                  // every wave is done with the v tile
+            if (active) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Ss[(rl + row_of(e)) * LR + 32 * wc + li] = x[e];
+            }
+            put_rows(Ys, rk);                 // the k tile takes the v tile's place
+            __syncthreads();
+        }
+        if (st + 1 < nsteps) prefetch_y(st + 1);
+        if (DS) {
+            // dQ rows i0 + rl, head columns 32 wc, over this tile's j
+            if (sl > 0 && j0 % 1024 == 0 && dirty) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) { qtot[e] = have ? qtot[e] + qacc[e] : qacc[e]; qacc[e] = 0.0f; }
+                have = true;
+                dirty = false;
+            }
+            const int cq = 32 * wc + li;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int64_t kb0 = j0 + 32 * hh, rb0 = i0 + rl;
+                const int ko = 32 * hh;
+                const int stt = kb0 < rb0 ? 1 : (kb0 == rb0 ? 2 : 0);
+                if (stt == 1) {
+                    dirty = true;
+#pragma unroll 8
+                    for (int p = 0; p < 16; ++p) {
+                        const int kk = ko + 2 * p + lk;
+                        qacc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ss[(rl + li) * LR + kk], Ys[kk * LR + cq], qacc, 0,
+                                                                    0, 0);
+                    }
+                } else if (stt == 2) {
+                    dirty = true;
+#pragma unroll 1
+                    for (int p = 0; p < 16; ++p) {
+                        const int kk = ko + 2 * p + lk;
+                        const v16f n = __builtin_amdgcn_mfma_f32_32x32x2f32(Ss[(rl + li) * LR + kk], Ys[kk * LR + cq],
+                                                                            qacc, 0, 0, 0);
+                        const int ka = 2 * p, kb = 2 * p + 1;
+                        const float as = Ss[(rl + ka) * LR + ko + ka], bs = Ys[(ko + ka) * LR + cq];
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int il = row_of(e);
+                            const float s1 = __builtin_fmaf(as, bs, qacc[e]);
+                            qacc[e] = il >= kb ? n[e] : (il == ka ? s1 : qacc[e]);
+                        }
+                    }
+                }
+            }
+            if (st + 1 < nsteps) prefetch_k(st + 1);
+            if (diag_tile) {   // the row tile's last step: fold, store dQ, reset
+                const uint32_t qo = (uint32_t)(i0 + rl) * (uint32_t)a.ldq + (uint32_t)cq;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    Q[qo + (uint32_t)row_of(e) * (uint32_t)a.ldq] = have ? (dirty ? qtot[e] + qacc[e] : qtot[e]) : qacc[e];
+                    qacc[e] = 0.0f;
+                    qtot[e] = 0.0f;
+                }
+                have = false;
+                dirty = false;
+            }
+        }
+    }
+}
+
 }  // namespace
+
+bool attn_rows_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* X, int64_t ldx, int64_t sXb,
+                    int64_t sXh, const float* Y, int64_t ldy, int64_t sYb, int64_t sYh, const float* S, int64_t ldS,
+                    int64_t sSb, int64_t sSh) {
+    if (hd != AV || T <= 0 || T % AV != 0 || ldS != T || batch < 1 || H < 1 || batch % H) return false;
+    // lane offsets inside one head are unsigned 32-bit element counts
+    const int64_t lim = (int64_t)1 << 32;
+    if (T * T >= lim || T * ldx >= lim || T * ldy >= lim) return false;
+    auto al = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+    return al(X) && al(Y) && al(S) && ldx % 4 == 0 && sXb % 4 == 0 && sXh % 4 == 0 && ldy % 4 == 0 && sYb % 4 == 0 &&
+           sYh % 4 == 0 && sSb % 4 == 0 && sSh % 4 == 0;
+}
+
+int attn_rows(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* X, int64_t ldx, int64_t sXb, int64_t sXh,
+              const float* Y, int64_t ldy, int64_t sYb, int64_t sYh, float* S, int64_t ldS, int64_t sSb, int64_t sSh,
+              float scale, const float* P, const float* D, const float* K, int64_t ldk, int64_t sKb, int64_t sKh,
+              float* dQ, int64_t ldq, int64_t sQb, int64_t sQh, hipStream_t s) {
+    if (!attn_rows_fits(T, hd, batch, H, X, ldx, sXb, sXh, Y, ldy, sYb, sYh, S, ldS, sSb, sSh)) return -2;
+    const bool ds = P != nullptr;
+    if (ds && (!D || !K || !dQ || ((uintptr_t)K & 15u) || ldk % 4 || sKb % 4 || sKh % 4 ||
+               T * ldk >= ((int64_t)1 << 32) || T * ldq >= ((int64_t)1 << 32)))
+        return -2;
+    const int64_t npairs = (T / AV + 1) / 2;
+    RowsArgs a{T, H, npairs, X, ldx, sXb, sXh, Y, ldy, sYb, sYh, S, sSb, sSh, scale,
+               P, D, K, ldk, sKb, sKh, dQ, ldq, sQb, sQh};
+    const dim3 grid((unsigned)(npairs * batch));
+    if (ds) k_attn_rows<true><<<grid, 256, 0, s>>>(a);
+    else k_attn_rows<false><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
                   int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh) {

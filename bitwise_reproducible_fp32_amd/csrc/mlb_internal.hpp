@@ -77,6 +77,24 @@ const char* gemm_last_kernel();
 // blk: C is stored in the tiled layout (ldc = T, a multiple of 32).
 // P and D non-null (scaled 0): softmax backward in the epilogue, C(i,j) =
 // (P(i,j) * (t(i,j) - D[z*T + i])) * ds_scale, with P laid out as C.
+int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
+           const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
+           int scaled, float scale, int blk, const float* P, const float* D, float ds_scale, hipStream_t s);
+
+// Lower-triangle row-strip kernels for 64-wide heads (mlb_attn.hip), S tiled
+// [T, T] per head with row length ldS == T. P == nullptr: S = (X . Y) * scale
+// for j <= i (the scores, X = q, Y = k). P != nullptr: t = X . Y with X = dO,
+// Y = v; S = dS = (P * (t - D_i)) * scale; and dQ = sum over j <= i of
+// dS_ij K_j (G1024), stored to dQ. Returns -2 when the shape is not one it
+// runs (the caller then uses tri_nt and the general contraction).
+bool attn_rows_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* X, int64_t ldx, int64_t sXb,
+                    int64_t sXh, const float* Y, int64_t ldy, int64_t sYb, int64_t sYh, const float* S, int64_t ldS,
+                    int64_t sSb, int64_t sSh);
+int attn_rows(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* X, int64_t ldx, int64_t sXb, int64_t sXh,
+              const float* Y, int64_t ldy, int64_t sYb, int64_t sYh, float* S, int64_t ldS, int64_t sSb, int64_t sSh,
+              float scale, const float* P, const float* D, const float* K, int64_t ldk, int64_t sKb, int64_t sKh,
+              float* dQ, int64_t ldq, int64_t sQb, int64_t sQh, hipStream_t s);
+
 // Causal contraction of 64-wide heads against the tiled attention matrix P
 // ([T, T] per head in 32x32 tiles, row length ldp == T): kr 1 C[i] = sum over
 // k <= i of P[i][k] B[k], kr 2 C[j] = sum over k >= j of P[k][j] B[k], the
@@ -88,9 +106,6 @@ bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* 
 int attn_av(int kr, int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
             int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb,
             int64_t sCh, hipStream_t s);
-int tri_nt(int64_t T, int64_t K, int64_t batch, int64_t H, const float* A, int64_t lda, int64_t sAb, int64_t sAh,
-           const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb, int64_t sCh,
-           int scaled, float scale, int blk, const float* P, const float* D, float ds_scale, hipStream_t s);
 
 // Row and elementwise kernels (mlb_ops.hip). All return 0 or a negative value
 // on invalid sizes; they launch on stream s and never synchronise.
