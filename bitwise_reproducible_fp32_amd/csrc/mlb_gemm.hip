@@ -509,6 +509,41 @@ __global__ __launch_bounds__(256) void k_fold(const float* __restrict__ part, in
     epilogue_store(a, a.mode, a.C, idx / N, idx % N, t);
 }
 
+// The same fold for four adjacent outputs of a row per thread (N % 4 == 0,
+// 16-byte aligned partials and rows): float4 traffic, and the partials of up
+// to 8 chunks loaded before the first addition, which is still in chunk order.
+__global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, int64_t nch, int64_t M, int64_t N,
+                                               KArgs a) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t MN = M * N, idx = q * 4;
+    if (idx >= MN) return;
+    const float4* p4 = reinterpret_cast<const float4*>(part);
+    const int64_t MN4 = MN / 4;
+    float4 t = p4[q];
+    for (int64_t c0 = 1; c0 < nch; c0 += 8) {
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (c0 + u < nch) x[u] = p4[(c0 + u) * MN4 + q];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (c0 + u < nch) { t.x = t.x + x[u].x; t.y = t.y + x[u].y; t.z = t.z + x[u].z; t.w = t.w + x[u].w; }
+    }
+    const int64_t i = idx / N, j = idx % N;
+    float* c = a.C + i * a.ldc + j;
+    float4 r = t;
+    if (a.mode == 1) {
+        const float4 o = *reinterpret_cast<const float4*>(c);
+        r.x = o.x + t.x; r.y = o.y + t.y; r.z = o.z + t.z; r.w = o.w + t.w;
+    } else if (a.mode == 2) {
+        r.x = t.x * a.scale; r.y = t.y * a.scale; r.z = t.z * a.scale; r.w = t.w * a.scale;
+    } else if (a.mode == 3) {
+        const float4 o = *reinterpret_cast<const float4*>(a.R + i * a.ldc + j);
+        r.x = o.x + t.x; r.y = o.y + t.y; r.z = o.z + t.z; r.w = o.w + t.w;
+    }
+    *reinterpret_cast<float4*>(c) = r;
+}
+
 struct Cfg { int wm, wn; };
 
 thread_local char g_launched[96];
@@ -751,7 +786,10 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
         std::memcpy(main_kernel, g_launched, sizeof g_launched);
         std::snprintf(g_launched, sizeof g_launched, "k_fold");
         t.begin();
-        k_fold<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p.scratch, nsplit, d.M, d.N, a);
+        const bool v4 = d.N % 4 == 0 && d.ldc % 4 == 0 && aligned16(d.C) && aligned16(p.scratch) &&
+                        (d.mode != 3 || aligned16(d.R));
+        if (v4) k_fold4<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(p.scratch, nsplit, d.M, d.N, a);
+        else k_fold<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p.scratch, nsplit, d.M, d.N, a);
         // partials read, output written (and read when accumulating)
         t.end(0.0, 4.0 * (double)n * (double)(nsplit + 1 + (d.mode == 1 || d.mode == 3 ? 1 : 0)));
         std::memcpy(g_launched, main_kernel, sizeof g_launched);

@@ -276,22 +276,48 @@ __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* 
         if (lane == 0) atomicOr(err, 2);
         y = 0;
     }
+    // Each lane walks v = lane, lane + 64, ... in ascending order (the W64
+    // rule); U of its elements are loaded before any is used, so that U loads
+    // per lane are in flight, and then taken in order.
+    constexpr int U = 8;
+    const int64_t vfull = lane + (V - lane) / (64 * U) * (64 * U);   // first v of the tail
     float m = -__builtin_inff();
-    for (int64_t v = lane; v < V; v += 64) m = max_keep(m, l[v]);
+    for (int64_t v = lane; v < vfull; v += 64 * U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = l[v + 64 * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) m = max_keep(m, x[u]);
+    }
+    for (int64_t v = vfull; v < V; v += 64) m = max_keep(m, l[v]);
     m = wave_tree_max(m);
     float acc = 0.0f;
-    for (int64_t v = lane; v < V; v += 64) acc = acc + exp_p(l[v] - m);
+    for (int64_t v = lane; v < vfull; v += 64 * U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = l[v + 64 * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = acc + exp_p(x[u] - m);
+    }
+    for (int64_t v = vfull; v < V; v += 64) acc = acc + exp_p(l[v] - m);
     const float Z = wave_tree_sum(acc);
     const float ly = l[y];
     if (lane == 0) loss_rows[n] = log_p(Z) - (ly - m);
     if (!dl) return;
     const float rz = 1.0f / Z;
-    float* o = dl + n * ld;
-    for (int64_t v = lane; v < V; v += 64) {
-        const float p = exp_p(l[v] - m) * rz;
-        const float t = (v == y) ? (p - 1.0f) : p;
-        o[v] = t * invN;
+    float* o = dl + n * ld;   // may be the logits themselves: each element is read before it is written
+    auto grad = [&](int64_t v, float x) -> float {
+        const float p = exp_p(x - m) * rz;
+        return ((v == y) ? (p - 1.0f) : p) * invN;
+    };
+    for (int64_t v = lane; v < vfull; v += 64 * U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = l[v + 64 * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) o[v + 64 * u] = grad(v + 64 * u, x[u]);
     }
+    for (int64_t v = vfull; v < V; v += 64) o[v] = grad(v, l[v]);
 }
 
 // Greedy choice, one wavefront per selected row r (row index r * row_step +
