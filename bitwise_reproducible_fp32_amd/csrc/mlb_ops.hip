@@ -86,33 +86,64 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict_
     }
 }
 
-// Gain gradient partials: part[ch][c] = fma chain over rows n of chunk ch
-// (1024 rows) of dy[n,c] * (x[n,c] * r[n]), from +0 in ascending n. There are
-// only d * chunks chains, so each lane issues the loads of 32 rows before it
-// runs their 32 dependent fmas, keeping many loads in flight per lane.
-constexpr int DW_ROWS = 32;
-__global__ __launch_bounds__(64) void k_rmsnorm_dw_part(const float* __restrict__ dy, const float* __restrict__ x,
+// Per-chunk column partials of the gain gradient: for column c and chunk ch
+// (rows [1024 ch, 1024 ch + 1024)), part[ch][c] is an fma chain from +0 over
+// the chunk's rows in ascending order of dy[n][c] * (x[n][c] * r[n]). There
+// are only d * chunks serial chains, so a workgroup owns 64 columns of one
+// chunk: all four waves stage 128-row blocks of dy and x * r in LDS (two
+// buffers, the next block loading while the current one is used) and wave 0
+// runs the 64 column chains through them.
+constexpr int DW_RB = 128;
+__global__ __launch_bounds__(256) void k_rmsnorm_dw_part(const float* __restrict__ dy, const float* __restrict__ x,
                                                         const float* __restrict__ r, int64_t rows, int64_t d,
                                                         float* __restrict__ part) {
-    const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    const int64_t ch = blockIdx.y;
+    __shared__ float sy[2][DW_RB][65], sx[2][DW_RB][65];
+    const int tid = threadIdx.x, col = tid & 63, rsub = tid >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + col;
     const bool live = c < d;
-    const int64_t cc = live ? c : 0;
-    const int64_t n0 = ch * KC, n1 = (n0 + KC < rows) ? n0 + KC : rows;
-    float acc = 0.0f;
-    int64_t n = n0;
-    for (; n + DW_ROWS <= n1; n += DW_ROWS) {
-        float vy[DW_ROWS], vx[DW_ROWS];
+    const int64_t n0 = (int64_t)blockIdx.y * KC, n1 = (n0 + KC < rows) ? n0 + KC : rows;
+    const int64_t nb = (n1 - n0 + DW_RB - 1) / DW_RB;
+    float vy[DW_RB / 4], vx[DW_RB / 4];
+    // Unconditional loads from clamped positions (a guarded load became a
+    // branch with a wait per row): rows past the chunk are never taken by
+    // the chain and columns past d are never stored.
+    const int64_t cc = live ? c : d - 1;
+    auto load = [&](int64_t b) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < DW_ROWS; ++q) {
-            vy[q] = dy[(n + q) * d + cc];
-            vx[q] = x[(n + q) * d + cc] * r[n + q];
+        for (int q = 0; q < DW_RB / 4; ++q) {
+            int64_t n = n0 + b * DW_RB + rsub + 4 * q;
+            n = n < n1 ? n : n1 - 1;
+            vy[q] = dy[n * d + cc];
+            vx[q] = x[n * d + cc] * r[n];
         }
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < DW_ROWS; ++q) acc = __builtin_fmaf(vy[q], vx[q], acc);
+        for (int q = 0; q < DW_RB / 4; ++q) {
+            sy[buf][rsub + 4 * q][col] = vy[q];
+            sx[buf][rsub + 4 * q][col] = vx[q];
+        }
+    };
+    float acc = 0.0f;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int64_t b = 0; b < nb; ++b) {
+        if (b + 1 < nb) load(b + 1);
+        if (tid < 64) {
+            const int64_t len = (n1 - n0 - b * DW_RB) < DW_RB ? (n1 - n0 - b * DW_RB) : DW_RB;
+            const int buf = (int)(b & 1);
+            if (len == DW_RB) {
+#pragma unroll 16
+                for (int k = 0; k < DW_RB; ++k) acc = __builtin_fmaf(sy[buf][k][col], sx[buf][k][col], acc);
+            } else {
+                for (int k = 0; k < len; ++k) acc = __builtin_fmaf(sy[buf][k][col], sx[buf][k][col], acc);
+            }
+        }
+        if (b + 1 < nb) store((int)((b + 1) & 1));
+        __syncthreads();
     }
-    for (; n < n1; ++n) acc = __builtin_fmaf(dy[n * d + cc], x[n * d + cc] * r[n], acc);
-    if (live) part[ch * d + c] = acc;
+    if (tid < 64 && live) part[blockIdx.y * d + c] = acc;
 }
 
 // Left fold of per-chunk column partials, then dw = t (mode 0) or dw + t (mode 1).
@@ -398,11 +429,30 @@ __global__ __launch_bounds__(256) void k_scatter_segments(const uint64_t* __rest
     const uint32_t v = (uint32_t)(kq >> 32);
     if (q > 0 && (uint32_t)(key[q - 1] >> 32) == v) return;    // not the head of its segment
     float acc = src_init ? src_init[(int64_t)v * d + c] : 0.0f;
-    for (int64_t e = q; e < N; ++e) {
-        const uint64_t ke = key[e];
-        if ((uint32_t)(ke >> 32) != v || ke == ~0ull) break;
-        const int64_t n = (int64_t)(uint32_t)ke;
-        acc = acc + dh[n * d + c];
+    // the segment's terms in sorted order; keys and rows of the next U terms
+    // are fetched before the first of them is added
+    constexpr int U = 8;
+    for (int64_t e0 = q; e0 < N; e0 += U) {
+        // unconditional loads from clamped positions (a guarded load becomes a
+        // branch and a wait); terms outside the segment are never added
+        uint64_t ke[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ke[u] = key[(e0 + u < N) ? e0 + u : N - 1];
+        bool in[U];
+        float t[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            in[u] = e0 + u < N && ke[u] != ~0ull && (uint32_t)(ke[u] >> 32) == v;
+            const int64_t n = in[u] ? (int64_t)(uint32_t)ke[u] : (int64_t)(uint32_t)kq;
+            t[u] = dh[n * d + c];
+        }
+        bool more = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            more = more && in[u];   // keys are sorted: the segment ends at the first other key
+            if (more) acc = acc + t[u];
+        }
+        if (!more) break;
     }
     float* o = dst + (int64_t)v * d + c;
     *o = mode ? *o + acc : acc;
@@ -521,7 +571,7 @@ int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows
         return ok();
     }
     const int64_t nch = (rows + KC - 1) / KC;
-    k_rmsnorm_dw_part<<<dim3(blocks(d, 64), (unsigned)nch), 64, 0, s>>>(dy, x, r, rows, d, part);
+    k_rmsnorm_dw_part<<<dim3(blocks(d, 64), (unsigned)nch), 256, 0, s>>>(dy, x, r, rows, d, part);
     k_fold_cols<<<blocks(d, 256), 256, 0, s>>>(part, nch, d, dw, mode);
     return ok();
 }
