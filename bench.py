@@ -41,14 +41,15 @@ def flops_per_token(cfg: dict) -> float:
 
 
 # Source files whose change invalidates measured HBM traffic of a kernel family.
-_KERNEL_SOURCES = {"k_gemm": "mlb_gemm.hip", "k_tri_nt": "mlb_attn.hip"}
+_KERNEL_SOURCES = {"k_gemm": "mlb_gemm.hip", "k_tri_nt": "mlb_attn.hip", "k_attn_av": "mlb_attn.hip",
+                   "k_attn_rows": "mlb_attn.hip"}
 
 
 def kernel_source_digest(kernel: str) -> str:
     import hashlib
     csrc = os.path.join(ROOT, "bitwise_reproducible_fp32_amd", "csrc")
     fam = kernel.split("<")[0].strip()
-    files = [_KERNEL_SOURCES.get(fam, "mlb_ops.hip"), "mlb_internal.hpp", "mlb_device.hpp"]
+    files = [_KERNEL_SOURCES.get(fam, "mlb_ops.hip"), "mlb_device.hpp"]   # the kernel's code and its device helpers
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
