@@ -41,7 +41,9 @@ struct TriArgs {
 __global__ __launch_bounds__(256) void k_tri_nt(TriArgs a) {
     __shared__ float As[TT * LD];
     __shared__ float Bs[TT * LD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform across the wave: saying so lets per-wave
+    // branches be scalar branches instead of exec-mask divergence
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     const int lk = lane >> 5, li = lane & 31;
     // XCD-aware order (whole heads per XCD), then the triangular tile index
@@ -198,7 +200,9 @@ void k_attn_av(AvArgs a) {
     constexpr int ALD = KR == 1 ? AV + 1 : AV_BLD;
     __shared__ float As[AV * ALD];
     __shared__ float Bs[AV * AV_BLD];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform across the wave: saying so lets per-wave
+    // branches be scalar branches instead of exec-mask divergence
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave & 1, wc = wave >> 1;   // the wave's 32-row and 32-column block
     const int lk = lane >> 5, li = lane & 31;
     const int64_t lb = xcd_logical_block();   // whole heads per XCD: B stays in one L2
@@ -217,16 +221,20 @@ void k_attn_av(AvArgs a) {
     // float4 captured by the lambdas was placed in scratch memory, which made
     // every load wait for its data at once
     float ra[16], rb[16];
+    // Addresses: a workgroup-uniform base plus an unsigned 32-bit lane offset
+    // (every offset inside one head is below 2^32 elements).
     auto load = [&](int64_t st) __attribute__((always_inline)) {
         const int64_t t = st < na ? ta : tb;
-        const int64_t k0 = first_k(t) + AV * (st < na ? st : st - na), r0 = t * AV;
+        const uint32_t k0 = (uint32_t)(first_k(t) + AV * (st < na ? st : st - na)), r0 = (uint32_t)(t * AV);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int q = tid + 256 * s, b = q >> 8, w = q & 255;
             // P tile (b >> 1, b & 1) of the stage: KR 1 (rows r0.., k0..), KR 2 (rows k0.., cols r0..)
-            const int64_t pr_ = (KR == 1 ? r0 : k0) / 32 + (b >> 1), pc_ = (KR == 1 ? k0 : r0) / 32 + (b & 1);
-            const float4 va = *reinterpret_cast<const float4*>(P + ((pr_ * ptr + pc_) << 10) + w * 4);
-            const float4 vb = *reinterpret_cast<const float4*>(Bm + (k0 + (q >> 4)) * a.ldb + (q & 15) * 4);
+            const uint32_t pr_ = (KR == 1 ? r0 : k0) / 32 + (uint32_t)(b >> 1);
+            const uint32_t pc_ = (KR == 1 ? k0 : r0) / 32 + (uint32_t)(b & 1);
+            const float4 va = *reinterpret_cast<const float4*>(P + (((pr_ * (uint32_t)ptr + pc_) << 10) + (uint32_t)w * 4));
+            const float4 vb = *reinterpret_cast<const float4*>(
+                Bm + ((k0 + (uint32_t)(q >> 4)) * (uint32_t)a.ldb + (uint32_t)(q & 15) * 4));
             ra[4 * s + 0] = va.x; ra[4 * s + 1] = va.y; ra[4 * s + 2] = va.z; ra[4 * s + 3] = va.w;
             rb[4 * s + 0] = vb.x; rb[4 * s + 1] = vb.y; rb[4 * s + 2] = vb.z; rb[4 * s + 3] = vb.w;
         }
@@ -302,11 +310,11 @@ void k_attn_av(AvArgs a) {
         }
         const bool last = (st + 1 == nsteps) || (st + 1 == na);
         if (last) {   // the tile's outputs: fold the last chunk, store, reset
-            float* Ct = C + (t * AV + rl) * a.ldc + 32 * wc + li;
+            const uint32_t co = (uint32_t)(t * AV + rl) * (uint32_t)a.ldc + (uint32_t)(32 * wc + li);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float v = have ? (dirty ? tot[e] + acc[e] : tot[e]) : acc[e];
-                Ct[(int64_t)(8 * (e >> 2) + 4 * lk + (e & 3)) * a.ldc] = v;
+                C[co + (uint32_t)(8 * (e >> 2) + 4 * lk + (e & 3)) * (uint32_t)a.ldc] = v;
                 acc[e] = 0.0f;
                 tot[e] = 0.0f;
             }
@@ -350,7 +358,9 @@ void k_attn_rows(RowsArgs a) {
     __shared__ float Ys[AV * LR];             // Y tile [j][h], then (dS) the k tile [j][h]
     __shared__ float Ss[DS ? AV * LR : 1];    // dS tile [i][j] for the dQ contraction
     __shared__ float Dv[DS ? AV : 1];         // D of the strip's rows
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform across the wave: saying so lets per-wave
+    // branches be scalar branches instead of exec-mask divergence
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wr = wave & 1, wc = wave >> 1;
     const int lk = lane >> 5, li = lane & 31;
     const int64_t lb = xcd_logical_block();
@@ -563,6 +573,7 @@ int attn_rows(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* X, i
 bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
                   int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh) {
     if (hd != AV || T <= 0 || T % AV != 0 || ldp != T || batch < 1 || H < 1 || batch % H) return false;
+    if (T * T >= ((int64_t)1 << 32) || T * ldb >= ((int64_t)1 << 32)) return false;   // 32-bit lane offsets
     return ((uintptr_t)P & 15u) == 0 && ((uintptr_t)B & 15u) == 0 && ldb % 4 == 0 && sBb % 4 == 0 && sBh % 4 == 0 &&
            sPb % 4 == 0 && sPh % 4 == 0;
 }

@@ -239,3 +239,59 @@ def test_safetensors_export_after_training():
     ref = TF.forward_logits(ctx, t, x.reshape(cfg["batch"], cfg["seq_len"])).reshape(N, V).numpy()
     assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
     m.close()
+
+
+def _oracle_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def test_c4_one_micro_batch_bit_exact():
+    """The 162M decoder at its full size, in the launch configuration bench.py
+    times (one stream): the loss, the whole accumulated gradient after one
+    micro-batch, and parameters and moments after AdamW equal the oracle's bit
+    for bit (the oracle takes about 20 s on 16 host threads)."""
+    import time
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c4")
+    init = I.init_params(cfg)
+    x, y = I.batch_for("c4", cfg, 1, 0)
+    g = mlb.Model(cfg, init)
+    g.set_overlap(False)
+    lg = g.forward_loss(dev(x.astype(np.int32)), dev(y.astype(np.int32)))
+    g.backward()
+    lr = I.lr_at("c4", 1)
+    G = g.read(mlb.GRAD)
+    g.adamw_step(lr)
+    got = {w: g.read(w) for w in (mlb.PARAMS, mlb.ADAM_M, mlb.ADAM_V)}
+    g.close()
+    oracle.set_threads(_oracle_threads())
+    t0 = time.time()
+    o = oracle.Model(cfg, init)
+    lo = o.forward(x, y)
+    o.backward()
+    print(f"oracle forward+backward of 8192 tokens: {time.time() - t0:.1f} s", flush=True)
+    assert np.float32(lg).tobytes() == np.float32(lo).tobytes(), (lg, lo)
+    assert_bits("c4 gradient after one micro-batch", G, o.grad)
+    o.adamw(lr)
+    for w, name in ((mlb.PARAMS, "params"), (mlb.ADAM_M, "m"), (mlb.ADAM_V, "v")):
+        assert_bits(f"c4 {name} after AdamW", got[w], o.read(w))
+
+
+def test_c4_stream_schedules_agree():
+    """At full size, the two backward schedules (one stream, or weight-gradient
+    work on the second stream) give the same gradient bits over two
+    micro-batches (a property that holds at any size)."""
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c4")
+    init = I.init_params(cfg)
+    xs = [I.batch_for("c4", cfg, 2, mb) for mb in range(2)]
+    out = []
+    for overlap in (False, True):
+        m = mlb.Model(cfg, init)
+        m.set_overlap(overlap)
+        for x, y in xs:
+            m.forward_loss(dev(x.astype(np.int32)), dev(y.astype(np.int32)))
+            m.backward()
+        out.append(m.read(mlb.GRAD))
+        m.close()
+    assert_bits("c4 gradient, one stream against two", out[1], out[0])
