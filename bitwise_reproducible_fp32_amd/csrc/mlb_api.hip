@@ -573,9 +573,15 @@ mlb_status forward(mlb_model* M, int mode = 0) {
     for (int64_t l = 0; l < s.L; ++l) {
         OP("rmsnorm_fwd", f4 * (2 * N * d + N + d),
            mlb::rmsnorm_fwd(M->h[l], M->p + M->o_w1[l], N, d, M->cfg.rms_eps, M->xn1[l], M->r1[l], st));
-        RUN("qkv_fwd", lin(N, 3 * d, d, M->xn1[l], d, true, M->p + M->o_qkv[l], d, true, M->qkv[l], 3 * d, 0));
-        OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
-        OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+        mlb::GemmDesc qkv = lin(N, 3 * d, d, M->xn1[l], d, true, M->p + M->o_qkv[l], d, true, M->qkv[l], 3 * d, 0);
+        if (hd == 64) {   // q and k rotated in the contraction's epilogue
+            qkv.rope_cos = M->cosv; qkv.rope_sin = M->sinv; qkv.rope_T = T; qkv.rope_cols = 2 * d;
+        }
+        RUN("qkv_fwd", qkv);
+        if (hd != 64) {
+            OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l], s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+            OP("rope_fwd", f4 * 2 * N * d, mlb::rope(M->qkv[l] + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 0, st));
+        }
         // S = (q . k) * scale, j <= i
         const mlb_status sr = run_rows(M, "attn_scores", M->qkv[l], 3 * d, M->qkv[l] + d, 3 * d, M->P[l],
                                        M->attn_scale);
@@ -735,9 +741,13 @@ mlb_status backward(mlb_model* M) {
         dk.A = M->dP; dk.lda = T; dk.a_kc = false; dk.sAb = H * T * T; dk.sAh = T * T;
         dk.B = M->qkv[l]; dk.ldb = 3 * d; dk.b_kc = false; dk.sBb = T * 3 * d; dk.sBh = hd;
         dk.C = dqkv + d; dk.ldc = 3 * d; dk.sCb = T * 3 * d; dk.sCh = hd;
+        // the paired-tile kernel rotates dk back in its epilogue
+        const bool dk_rope = mlb::attn_av_fits(T, hd, BH, H, M->dP, T, H * T * T, T * T, M->qkv[l], 3 * d, T * 3 * d, hd);
+        if (dk_rope) { dk.rope_cos = M->cosv; dk.rope_sin = M->sinv; }
         RUN("attn_dk", dk);
         OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
-        OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        if (!dk_rope)
+            OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
         CHK(to_side());
         RUN("qkv_dw", lin(3 * d, d, N, dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1));
         CHK(ring_read(M, DQKV, kq));

@@ -189,7 +189,31 @@ struct AvArgs {
     const float* A; int64_t sAb, sAh;
     const float* B; int64_t ldb, sBb, sBh;
     float* C; int64_t ldc, sCb, sCh;
+    const float* rope_cos;   // non-null: inverse rotary embedding of the output rows (positions) before the store
+    const float* rope_sin;
 };
+
+// Inverse rotary embedding of a wave's 32x32 output block at the end of a row
+// tile: the pairs (i, i + 32) of a 64-wide head sit in the waves of column
+// halves 0 and 1, so the block passes through LDS (buf, 64 rows of stride ld)
+// and each lane takes its partner from the other half. The arithmetic is the
+// rope kernel's backward rotation, element by element. Every wave of the
+// workgroup calls it together.
+__device__ __forceinline__ void rope_bwd_block(float (&q)[16], float* buf, int ld, int rl, int wc, int li, int lk,
+                                               int64_t row0, const float* cosv, const float* sinv) {
+    __syncthreads();   // every wave is done reading buf as an operand
+#pragma unroll
+    for (int e = 0; e < 16; ++e) buf[(rl + 8 * (e >> 2) + 4 * lk + (e & 3)) * ld + 32 * wc + li] = q[e];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * lk + (e & 3);
+        const float other = buf[(rl + r) * ld + 32 * (1 - wc) + li];
+        const int64_t t = row0 + r;
+        const float c = cosv[t * 32 + li], sn = sinv[t * 32 + li];
+        q[e] = wc == 0 ? (q[e] * c) + (other * sn) : (q[e] * c) - (other * sn);
+    }
+}
 
 template <int KR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
@@ -309,15 +333,18 @@ void k_attn_av(AvArgs a) {
             }
         }
         const bool last = (st + 1 == nsteps) || (st + 1 == na);
-        if (last) {   // the tile's outputs: fold the last chunk, store, reset
-            const uint32_t co = (uint32_t)(t * AV + rl) * (uint32_t)a.ldc + (uint32_t)(32 * wc + li);
+        if (last) {   // the tile's outputs: fold the last chunk, (rotate,) store, reset
+            float v[16];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float v = have ? (dirty ? tot[e] + acc[e] : tot[e]) : acc[e];
-                C[co + (uint32_t)(8 * (e >> 2) + 4 * lk + (e & 3)) * (uint32_t)a.ldc] = v;
+                v[e] = have ? (dirty ? tot[e] + acc[e] : tot[e]) : acc[e];
                 acc[e] = 0.0f;
                 tot[e] = 0.0f;
             }
+            if (a.rope_cos) rope_bwd_block(v, As, ALD, rl, wc, li, lk, t * AV + rl, a.rope_cos, a.rope_sin);
+            const uint32_t co = (uint32_t)(t * AV + rl) * (uint32_t)a.ldc + (uint32_t)(32 * wc + li);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) C[co + (uint32_t)(8 * (e >> 2) + 4 * lk + (e & 3)) * (uint32_t)a.ldc] = v[e];
             have = false;
             dirty = false;
         }
@@ -580,11 +607,12 @@ bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* 
 
 int attn_av(int kr, int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
             int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb,
-            int64_t sCh, hipStream_t s) {
+            int64_t sCh, const float* rope_cos, const float* rope_sin, hipStream_t s) {
     if (kr != 1 && kr != 2) return -1;
+    if ((rope_cos != nullptr) != (rope_sin != nullptr)) return -1;
     if (!attn_av_fits(T, hd, batch, H, P, ldp, sPb, sPh, B, ldb, sBb, sBh)) return -2;
     const int64_t npairs = (T / AV + 1) / 2;
-    AvArgs a{T, H, npairs, P, sPb, sPh, B, ldb, sBb, sBh, C, ldc, sCb, sCh};
+    AvArgs a{T, H, npairs, P, sPb, sPh, B, ldb, sBb, sBh, C, ldc, sCb, sCh, rope_cos, rope_sin};
     const dim3 grid((unsigned)(npairs * batch));
     if (kr == 1) k_attn_av<1><<<grid, 256, 0, s>>>(a);
     else k_attn_av<2><<<grid, 256, 0, s>>>(a);

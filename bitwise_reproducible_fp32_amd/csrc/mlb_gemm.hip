@@ -53,6 +53,9 @@ struct KArgs {
     // over row tiles tm_lo.. (launched in chunk order; rows whose first chunk
     // it is store, later chunks add to C)
     int64_t chunk, tm_lo;
+    const float* rope_cos;   // non-null: rotary embedding of columns [0, rope_cols) in the epilogue
+    const float* rope_sin;
+    int64_t rope_T, rope_cols;
 };
 
 // Offset of element (r, c) of a matrix stored as 32x32 tiles, each 4 KiB
@@ -433,6 +436,19 @@ void k_gemm(KArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) { x0[e] = x0[e] * a.scale; x1[e] = x1[e] * a.scale; }
         }
+        // rotary embedding: this wave's 64 columns are one head, and the lane
+        // holds column i of it in x0 and column i + 32 in x1
+        if (WN == 2 && a.rope_cos && !a.split && j0 + 64 * wn < a.rope_cols) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t t = row(e) % a.rope_T;
+                const float c = a.rope_cos[t * 32 + li], sn = a.rope_sin[t * 32 + li];
+                const float r0 = (x0[e] * c) - (x1[e] * sn);
+                const float r1 = (x1[e] * c) + (x0[e] * sn);
+                x0[e] = r0;
+                x1[e] = r1;
+            }
+        }
         if (interior) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -700,6 +716,7 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     a.H = d.H; a.sAb = d.sAb; a.sAh = d.sAh; a.sBb = d.sBb; a.sBh = d.sBh; a.sCb = d.sCb; a.sCh = d.sCh;
     a.outmask = d.outmask; a.mode = d.mode; a.krange = d.krange; a.scale = d.scale;
     a.split = 0; a.part = nullptr; a.chunk = -1; a.tm_lo = 0;
+    a.rope_cos = d.rope_cos; a.rope_sin = d.rope_sin; a.rope_T = d.rope_T; a.rope_cols = d.rope_cols;
     // The causal attention contractions of 64-wide heads (tiled P, square,
     // one segment) have their own kernel when the plan leaves the choice open.
     if (p.tile < 0 && p.split < 0 && !p.simple && d.a_blk && d.mode == 0 && !d.outmask && !d.b_kc &&
@@ -708,7 +725,7 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
         std::snprintf(g_launched, sizeof g_launched, "k_attn_av<%d>", d.krange);
         t.begin();
         const int r = attn_av(d.krange, d.M, d.N, d.batch, d.H, d.A, d.lda, d.sAb, d.sAh, d.B, d.ldb, d.sBb, d.sBh,
-                              d.C, d.ldc, d.sCb, d.sCh, s);
+                              d.C, d.ldc, d.sCb, d.sCh, d.rope_cos, d.rope_sin, s);
         t.end(gemm_flops(d, 0, d.K), 0.0);
         return r;
     }
@@ -727,12 +744,16 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     bool vec = aligned16(d.A) && aligned16(d.B) && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
                d.sAb % 4 == 0 && d.sAh % 4 == 0 && d.sBb % 4 == 0 && d.sBh % 4 == 0;
     vec = vec && (d.a_kc ? up4(d.K) <= d.lda : up4(d.M) <= d.lda) && (d.b_kc ? up4(d.K) <= d.ldb : up4(d.N) <= d.ldb);
-    const bool split = want_split(d, p);
+    const bool rope = d.rope_cos != nullptr;
+    if (rope && (!d.rope_sin || d.rope_T <= 0 || d.rope_cols % 64 != 0 || d.rope_cols > d.N || d.mode != 0 ||
+                 d.krange != 0 || d.outmask || d.batch != 1 || p.simple || p.tile > 0 || p.split == 1))
+        return -1;
+    const bool split = !rope && want_split(d, p);
     // 128x128 tiles in general; 128x64 when 128x128 tiles would not fill the
     // chip once (fewer workgroups than 256 CUs x 3 resident); 256x64 for
     // 64-wide outputs; 128x64 for causal ranges (their work per row tile grows
     // along the diagonal)
-    int cfg = p.tile;
+    int cfg = rope ? 0 : p.tile;
     if (cfg < 0) {
         const int64_t wg128 = ((d.M + 127) / 128) * ((d.N + 127) / 128) * (split ? nchunks(d) : 1) * d.batch;
         cfg = d.krange != 0 ? 2 : (d.N <= 64 ? 1 : (wg128 < 768 ? 2 : 0));
@@ -770,7 +791,7 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     const bool mc = !split && nch > 1;
     t.begin();
     if (!launch_tiled(d, a, cfg, vec, mc, nsplit, s)) {
-        if (split) return -1;
+        if (split || rope) return -1;
         const int64_t n = d.M * d.N;
         const dim3 grid((unsigned)((n + 255) / 256), 1, (unsigned)d.batch);
         std::snprintf(g_launched, sizeof g_launched, "k_gemm_simple");

@@ -31,6 +31,14 @@ struct GemmDesc {
     int64_t sAb = 0, sAh = 0, sBb = 0, sBh = 0, sCb = 0, sCh = 0;
     int krange = 0, outmask = 0, mode = 0;
     float scale = 1.0f;
+    // Rotary embedding in the epilogue (mode 0, 64-wide heads): output columns
+    // [0, rope_cols) are heads of 64 whose pairs (i, i + 32) at position
+    // t = row mod rope_T are rotated by cos/sin[t][i] exactly as the rope
+    // kernel does. Forces 128x128 tiles (a wave's 64 columns are one head, and
+    // a lane holds both elements of its pairs) and no split.
+    const float* rope_cos = nullptr;
+    const float* rope_sin = nullptr;
+    int64_t rope_T = 0, rope_cols = 0;
 };
 
 // Tiled square layout of the attention matrices P and dS: element (r, c) of a
@@ -98,14 +106,15 @@ int attn_rows(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* X, i
 // Causal contraction of 64-wide heads against the tiled attention matrix P
 // ([T, T] per head in 32x32 tiles, row length ldp == T): kr 1 C[i] = sum over
 // k <= i of P[i][k] B[k], kr 2 C[j] = sum over k >= j of P[k][j] B[k], the
-// G1024 rule, mode 0 (mlb_attn.hip). Returns -2 when the shape is not one it
-// runs (hd != 64, T not a multiple of 64, misaligned operands): the caller
-// then uses the general contraction.
+// G1024 rule, mode 0 (mlb_attn.hip); rope_cos/rope_sin ([T][32] tables)
+// rotate the output rows back before the store. Returns -2 when the shape is
+// not one it runs (hd != 64, T not a multiple of 64, misaligned operands): the
+// caller then uses the general contraction.
 bool attn_av_fits(int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
                   int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh);
 int attn_av(int kr, int64_t T, int64_t hd, int64_t batch, int64_t H, const float* P, int64_t ldp, int64_t sPb,
             int64_t sPh, const float* B, int64_t ldb, int64_t sBb, int64_t sBh, float* C, int64_t ldc, int64_t sCb,
-            int64_t sCh, hipStream_t s);
+            int64_t sCh, const float* rope_cos, const float* rope_sin, hipStream_t s);
 
 // Row and elementwise kernels (mlb_ops.hip). All return 0 or a negative value
 // on invalid sizes; they launch on stream s and never synchronise.
