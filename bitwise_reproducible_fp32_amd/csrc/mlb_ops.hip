@@ -203,6 +203,9 @@ __global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t 
 
 // The same rule with the row held in registers (lane l owns j = l + 64m,
 // m < PER): one read and one write of the row instead of three and two.
+// Element j = lane + 64 m of row i sits at base + m * stride inside the
+// head's matrix (tiled: two 32-wide tiles further per m), as an unsigned
+// 32-bit offset (T * T < 2^32): one address register per lane.
 template <int PER>
 __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int64_t T, int blk) {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -211,11 +214,12 @@ __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int6
     const int64_t i = row % T;
     float* p = P + (row / T) * T * T;
     const int64_t n = i + 1;
+    const uint32_t base = (uint32_t)pos(blk, T, i, lane), stride = blk ? 2048u : 64u;
     float v[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         const int64_t j = lane + 64 * m;
-        v[m] = j < n ? p[pos(blk, T, i, j)] : 0.0f;
+        v[m] = j < n ? p[base + (uint32_t)m * stride] : 0.0f;
     }
     float mx = -__builtin_inff();
 #pragma unroll
@@ -234,7 +238,7 @@ __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int6
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         const int64_t j = lane + 64 * m;
-        if (j < n) p[pos(blk, T, i, j)] = v[m] * rz;
+        if (j < n) p[base + (uint32_t)m * stride] = v[m] * rz;
     }
 }
 
@@ -586,7 +590,7 @@ int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, cons
 }
 
 int softmax_causal(float* P, int64_t nbh, int64_t T, int blk, hipStream_t s) {
-    if (nbh < 0 || T < 0 || (blk && T % 32)) return -1;
+    if (nbh < 0 || T < 0 || (blk && T % 32) || T * T >= ((int64_t)1 << 32)) return -1;
     if (nbh * T == 0) return 0;
     if (T <= 512) k_softmax_reg<8><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T, blk);
     else if (T <= 2048) k_softmax_reg<32><<<blocks(nbh * T, 4), 256, 0, s>>>(P, nbh, T, blk);
