@@ -70,6 +70,7 @@ _SIGS = {
     "mlb_state_card": (i32, [vp, i32, vp]),
     "mlb_stats_enable": (i32, [vp, i32]),
     "mlb_stats_read": (i32, [vp, C.POINTER(Stat), i32, C.POINTER(i32)]),
+    "mlb_stats_sites": (i32, [vp, C.c_char_p]),
     "mlb_destroy": (i32, [vp]),
     "mlb_status_name": (C.c_char_p, [i32]),
     "mlb_last_error_message": (C.c_char_p, []),
@@ -278,6 +279,10 @@ class Model:
 
     def stats_enable(self, on: bool = True) -> None:
         check(lib().mlb_stats_enable(self.h, int(on)))
+
+    def stats_sites(self, sites=None) -> None:
+        """Time only these call sites (an iterable of names); None times all."""
+        check(lib().mlb_stats_sites(self.h, None if not sites else ",".join(sites).encode()))
 
     def stats(self) -> list[dict]:
         """Per-site launch statistics since stats_enable (see mlb_stats_read)."""

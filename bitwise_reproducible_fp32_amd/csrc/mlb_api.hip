@@ -258,6 +258,7 @@ struct mlb_model {
     int n_accum;
     float attn_scale, invN;
     bool stats_on = false;
+    std::vector<std::string> stats_sites;   // empty: every call site is timed
     std::vector<StatRec> pending;
     std::vector<hipEvent_t> free_events;
     std::map<std::string, StatAgg> agg;
@@ -432,8 +433,11 @@ mlb::GemmDesc lin(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, 
 // Optional per-launch timing with HIP events on the stream the launch runs on
 // (the caller's or the side stream), grouped by call site, with each launch's algorithmic work (FLOPs of the contraction's
 // valid pairs, or the minimal HBM bytes of a row/elementwise kernel).
-int64_t stat_begin(mlb_model* M) {
+int64_t stat_begin(mlb_model* M, const char* site) {
     if (!M->stats_on) return -1;
+    if (!M->stats_sites.empty() &&
+        std::find(M->stats_sites.begin(), M->stats_sites.end(), site) == M->stats_sites.end())
+        return -1;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (M->free_events.size() >= 2) {
         e0 = M->free_events.back(); M->free_events.pop_back();
@@ -477,7 +481,7 @@ struct GemmStatCtx {
 };
 void gemm_stat_begin(void* c) {
     auto* x = static_cast<GemmStatCtx*>(c);
-    x->ev = stat_begin(x->M);
+    x->ev = stat_begin(x->M, x->site);
 }
 void gemm_stat_end(void* c, const char* kernel, double flops, double bytes) {
     auto* x = static_cast<GemmStatCtx*>(c);
@@ -505,7 +509,7 @@ mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
 // A row or elementwise kernel with its algorithmic HBM bytes.
 #define OP(site, bytes, x)                                                           \
     do {                                                                             \
-        const int64_t ev_ = stat_begin(M);                                           \
+        const int64_t ev_ = stat_begin(M, site);                                     \
         const int r_ = (x);                                                          \
         stat_end(M, ev_, site, site, 0.0, (double)(bytes));                          \
         if (r_ != 0) return fail(MLB_E_DEVICE, "%s returned %d", #x, r_);            \
@@ -518,7 +522,7 @@ mlb_status run_tri(mlb_model* M, const char* site, int64_t T, int64_t hd, const 
                    const float* B, int64_t ldb, int64_t sBb, float* C, int scaled, float scale,
                    const float* P = nullptr, const float* D = nullptr, float ds_scale = 0.0f) {
     const Sizes& s = M->s;
-    const int64_t ev = stat_begin(M);
+    const int64_t ev = stat_begin(M, site);
     const int r = mlb::tri_nt(T, hd, s.B * s.H, s.H, A, lda, sAb, hd, B, ldb, sBb, hd, C, T, s.H * T * T, T * T,
                               scaled, scale, 1, P, D, ds_scale, M->cur);
     stat_end(M, ev, site, "k_tri_nt", 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd,
@@ -539,7 +543,7 @@ mlb_status run_rows(mlb_model* M, const char* site, const float* X, int64_t ldx,
                              T * T))
         return MLB_E_UNSUPPORTED;
     const double tri = 2.0 * (double)(s.B * s.H) * (double)T * (double)(T + 1) / 2.0 * (double)hd;
-    const int64_t ev = stat_begin(M);
+    const int64_t ev = stat_begin(M, site);
     const int r = mlb::attn_rows(T, hd, s.B * s.H, s.H, X, ldx, T * ldx, hd, Y, ldy, T * ldy, hd, S, T, s.H * T * T,
                                  T * T, scale, P, D, K, ldk, T * ldk, hd, dQ, ldq, T * ldq, hd, M->cur);
     stat_end(M, ev, site, P ? "k_attn_rows<dS,dQ>" : "k_attn_rows<S>", P ? 2.0 * tri : tri, 0.0);
@@ -1252,6 +1256,23 @@ mlb_status mlb_stats_enable(mlb_model* M, int on) {
     stat_resolve(M);
     M->agg.clear();
     M->stats_on = on != 0;
+    return MLB_OK;
+}
+
+mlb_status mlb_stats_sites(mlb_model* M, const char* sites) {
+    if (!M) return fail(MLB_E_INVALID_ARG, "null model");
+    M->stats_sites.clear();
+    if (!sites) return MLB_OK;
+    std::string cur;
+    for (const char* c = sites;; ++c) {
+        if (*c == ',' || *c == '\0') {
+            if (!cur.empty()) M->stats_sites.push_back(cur);
+            cur.clear();
+            if (*c == '\0') break;
+        } else {
+            cur += *c;
+        }
+    }
     return MLB_OK;
 }
 
