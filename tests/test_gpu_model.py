@@ -295,3 +295,34 @@ def test_c4_stream_schedules_agree():
         out.append(m.read(mlb.GRAD))
         m.close()
     assert_bits("c4 gradient, one stream against two", out[1], out[0])
+
+
+def test_stats_site_filter():
+    """mlb_stats_sites restricts the launch statistics to the named call sites,
+    and timing never changes the bits."""
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c0")
+    m = mlb.Model(cfg, I.init_params(cfg))
+    x, y = I.batch_for("c0", cfg, 1, 0)
+    xd, yd = dev(x.astype(np.int32)), dev(y.astype(np.int32))
+    m.stats_enable(True)
+    m.forward_loss(xd, yd)
+    m.backward()
+    every = {s["site"] for s in m.stats()}
+    m.stats_enable(False)
+    assert {"qkv_fwd", "head_fwd", "xent", "head_dw"} <= every
+    m.stats_sites(["qkv_fwd", "head_dw"])
+    m.stats_enable(True)
+    m.adamw_step(1e-3)
+    m.forward_loss(xd, yd)
+    m.backward()
+    some = {s["site"] for s in m.stats()}
+    assert some == {"qkv_fwd", "head_dw"}, some
+    m.stats_enable(False)
+    m.stats_sites(None)
+    g_timed = m.read(mlb.GRAD)
+    ref = mlb.Model(cfg, I.init_params(cfg))
+    ref.forward_loss(xd, yd); ref.backward(); ref.adamw_step(1e-3)
+    ref.forward_loss(xd, yd); ref.backward()
+    assert_bits("gradient with and without timing", g_timed, ref.read(mlb.GRAD))
+    m.close(); ref.close()
