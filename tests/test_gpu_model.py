@@ -326,3 +326,33 @@ def test_stats_site_filter():
     ref.forward_loss(xd, yd); ref.backward()
     assert_bits("gradient with and without timing", g_timed, ref.read(mlb.GRAD))
     m.close(); ref.close()
+
+
+@pytest.mark.parametrize("B,T", [(1, 1056), (2, 1088)])
+def test_routing_of_64_wide_heads(B, T):
+    """The 6-layer decoder's shape (64-wide heads) at two sequence lengths:
+    T = 1056 (a multiple of 32, not of 64) takes the general attention kernels
+    and the separate RoPE passes, T = 1088 the paired-tile and row-strip
+    kernels with RoPE in the contraction epilogues (17 row tiles, two
+    1024-chunks). Loss, gradient and the AdamW state equal the oracle's after
+    one micro-batch."""
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c3", batch=B, seq_len=T)
+    init = I.init_params(cfg)
+    rng = np.random.default_rng(T)
+    x = rng.integers(0, cfg["vocab"], (B, T)).astype(np.int32)
+    y = rng.integers(0, cfg["vocab"], (B, T)).astype(np.int32)
+    g = mlb.Model(cfg, init)
+    g.set_overlap(False)
+    lg = g.forward_loss(dev(x), dev(y))
+    g.backward()
+    G = g.read(mlb.GRAD)
+    g.adamw_step(1e-3)
+    o = oracle.Model(cfg, init)
+    lo = o.forward(x, y)
+    o.backward()
+    assert np.float32(lg).tobytes() == np.float32(lo).tobytes(), (lg, lo)
+    assert_bits(f"gradient T={T}", G, o.grad)
+    o.adamw(np.float32(1e-3))
+    assert_bits(f"params T={T}", g.read(mlb.PARAMS), o.read(mlb.PARAMS))
+    g.close()
