@@ -355,6 +355,119 @@ __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* 
     for (int64_t v = vfull; v < V; v += 64) o[v] = grad(v, l[v]);
 }
 
+// exp_p without branches, bit for bit the same function: the reduction and
+// polynomial run on 0 in place of a NaN or out-of-range input and the special
+// result is selected at the end; the scale 2^k is applied as (p * s1) * s2
+// with s2 = 1 in the normal range, where multiplying by 1 is exact. For code
+// that evaluates many exponentials per thread, where the branches of exp_p
+// would each hold an exec mask.
+__device__ __forceinline__ float exp_p_select(float x) {
+    const bool nan = x != x, hi = x >= u2f(0x42B17218u), lo = x <= u2f(0xC2CFF1B5u);
+    const float xs = (nan || hi || lo) ? 0.0f : x;
+    const float shifter = 12582912.0f;
+    const float t = xs * u2f(0x3FB8AA3Bu);
+    const float kf = (t + shifter) - shifter;
+    const int ki = (int)kf;
+    float r = __builtin_fmaf(-kf, u2f(0x3F317200u), xs);
+    r = __builtin_fmaf(-kf, u2f(0x35BFBE8Eu), r);
+    float p = u2f(0x39500D01u);
+    p = __builtin_fmaf(p, r, u2f(0x3AB60B61u));
+    p = __builtin_fmaf(p, r, u2f(0x3C088889u));
+    p = __builtin_fmaf(p, r, u2f(0x3D2AAAABu));
+    p = __builtin_fmaf(p, r, u2f(0x3E2AAAABu));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const bool big = ki > 127, small = ki < -126;
+    const float s1 = big ? u2f(0x7F000000u) : u2f((uint32_t)(small ? ki + 253 : ki + 127) << 23);
+    const float s2 = big ? 2.0f : (small ? u2f(0x00800000u) : 1.0f);
+    const float v = (p * s1) * s2;
+    return nan ? x : (hi ? __builtin_inff() : (lo ? 0.0f : v));
+}
+
+// Cross-entropy of a long row read from HBM once: a workgroup of XR_W waves
+// owns one row, and thread (w, lane) holds v = lane + 64 (w C + c), c < C,
+// in registers, so the row is read once and dl written once (the three-pass
+// kernel above reads it three times). The results are those of k_xent, bit
+// for bit:
+//  - m is the largest non-NaN entry. Any grouping gives that value; only the
+//    sign of a zero maximum can differ, and no later result depends on it
+//    (exp(x - m) and l_y - m give the same bits for m = +0 and m = -0).
+//  - e = exp(l - m) is computed once per entry and kept.
+//  - Z: each lane's chain adds its entries in ascending v from +0, wave 0's
+//    share first, then wave 1's, and so on (the running sum passes through
+//    LDS), then the same lane tree as k_xent. Positions past V hold +0, and
+//    adding +0 leaves the chain's value unchanged (it starts at +0 and only
+//    adds values >= +0 or NaN, so it is never -0).
+constexpr int XR_W = 8;
+template <int C>
+__global__ __launch_bounds__(64 * XR_W) void k_xent_row(const float* l_in, const int32_t* __restrict__ tg, int64_t V,
+                                                       int64_t ld, float invN, float* __restrict__ loss_rows,
+                                                       float* dl, int* err) {
+    __shared__ float wmax[XR_W];
+    __shared__ float chain[64];
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float* l = l_in + n * ld;
+    int64_t y = tg[n];
+    if (y < 0 || y >= V) {
+        if (tid == 0) atomicOr(err, 2);
+        y = 0;
+    }
+    const uint32_t vb = (uint32_t)lane + 64u * (uint32_t)(w * C);
+    // this lane's count of positions below V, and the c holding the target (or -1)
+    const int64_t rem = V - (int64_t)vb;
+    int nv = rem <= 0 ? 0 : (int)((rem + 63) / 64 < C ? (rem + 63) / 64 : C);
+    const int64_t ty = y - (int64_t)vb;
+    const int cy = (ty >= 0 && ty % 64 == 0 && ty / 64 < C) ? (int)(ty / 64) : -1;
+    // every read of the row happens before the first barrier; dl may be the
+    // logits themselves and is written only after the last one
+    const float ly = l[y];
+    // buffer accesses over the row's V entries: the hardware range check
+    // returns 0 for a load past V and drops such a store, so no lane needs a
+    // clamped address or a branch
+    const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc((void*)l, 0, (int)(V * 4), 0x00020000);
+    float e[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+        e[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (vb + 64u * (uint32_t)c) * 4u, 0, 0));
+#pragma unroll
+    for (int c = 0; c < C; ++c) e[c] = c < nv ? e[c] : -__builtin_inff();
+    // the position tests are made again below rather than kept as C lane masks
+    asm volatile("" : "+v"(nv));
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < C; ++c) m = max_keep(m, e[c]);
+    m = wave_tree_max(m);
+    if (lane == 0) wmax[w] = m;
+    __syncthreads();
+    m = wmax[0];
+#pragma unroll
+    for (int k = 1; k < XR_W; ++k) m = max_keep(m, wmax[k]);
+#pragma unroll
+    for (int c = 0; c < C; ++c) e[c] = exp_p_select(c < nv ? e[c] - m : -__builtin_inff());   // exp(-inf) = +0
+    for (int k = 0; k < XR_W; ++k) {
+        if (w == k) {
+            float acc = k == 0 ? 0.0f : chain[lane];
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc = acc + e[c];
+            chain[lane] = acc;
+        }
+        __syncthreads();
+    }
+    const float Z = wave_tree_sum(chain[lane]);
+    if (tid == 0) loss_rows[n] = log_p(Z) - (ly - m);
+    if (!dl) return;
+    const float rz = 1.0f / Z;
+    const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc((void*)(dl + n * ld), 0, (int)(V * 4), 0x00020000);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const float p = e[c] * rz;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((c == cy ? (p - 1.0f) : p) * invN), rout,
+                                              (vb + 64u * (uint32_t)c) * 4u, 0, 0);
+    }
+}
+
 // Greedy choice, one wavefront per selected row r (row index r * row_step +
 // row_off of a [rows, ld] matrix): the index of the largest of the first V
 // entries; NaN ranks below every number and ties go to the lowest index (a
@@ -495,7 +608,7 @@ __global__ __launch_bounds__(256) void k_unary(const float* __restrict__ x, floa
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const float v = x[i];
-    y[i] = which == 0 ? exp_p(v) : (which == 1 ? log_p(v) : sigmoid_p(v));
+    y[i] = which == 0 ? exp_p(v) : (which == 1 ? log_p(v) : (which == 2 ? sigmoid_p(v) : exp_p_select(v)));
 }
 
 __global__ __launch_bounds__(256) void k_zero(float* x, int64_t n) {
@@ -630,7 +743,13 @@ int cross_entropy(const float* logits, const int32_t* tg, int64_t N, int64_t V, 
     if (N < 0 || V <= 0 || ld < V) return -1;
     if (N == 0) return 0;
     const float invN = 1.0f / (float)N;
-    k_xent<<<blocks(N, 4), 256, 0, s>>>(logits, tg, N, V, ld, invN, loss_rows, dl, err);
+    // rows of 25,345..50,688 entries (the 50,257-token vocabulary) are held in
+    // registers by one workgroup each; other lengths take the three-pass kernel
+    constexpr int XR_C = 99;
+    if (V > 64 * XR_W * XR_C / 2 && V <= 64 * XR_W * XR_C && N < ((int64_t)1 << 31))
+        k_xent_row<XR_C><<<(unsigned)N, 64 * XR_W, 0, s>>>(logits, tg, V, ld, invN, loss_rows, dl, err);
+    else
+        k_xent<<<blocks(N, 4), 256, 0, s>>>(logits, tg, N, V, ld, invN, loss_rows, dl, err);
     return ok();
 }
 
@@ -672,7 +791,7 @@ int adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float b1,
 }
 
 int exp_array(const float* x, float* y, int64_t n, int which, hipStream_t s) {
-    if (n <= 0 || which < 0 || which > 2) return n == 0 ? 0 : -1;
+    if (n <= 0 || which < 0 || which > 3) return n == 0 ? 0 : -1;
     k_unary<<<blocks(n, 256), 256, 0, s>>>(x, y, n, which);
     return ok();
 }

@@ -100,7 +100,8 @@ mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N
 mlb_status mlb_prim_adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2,
                           float eps, float wd, int64_t t, void* hip_stream);
 
-/* Elementwise spellings: which 0 exp, 1 log, 2 sigmoid. */
+/* Elementwise spellings: which 0 exp, 1 log, 2 sigmoid, 3 exp in its branch-free
+ * form (the same bits as 0, as the cross-entropy of long rows evaluates it). */
 mlb_status mlb_prim_unary(const float* x, float* y, int64_t n, int which, void* hip_stream);
 
 /* Matrix-core probe: one FP32 MFMA per wavefront on lane-held operands, for

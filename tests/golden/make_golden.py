@@ -2,7 +2,8 @@
 
 Every value here comes from the CPU oracle (oracle/), run on the seeded inputs
 of bitwise_reproducible_fp32_amd.inputs; nothing is taken from the HIP path.
-Usage: python tests/golden/make_golden.py c0 c2 c3 [--threads N]
+Usage: python tests/golden/make_golden.py c0 c2 c3 c4 [--threads N]
+(c4, one full step of the 162M decoder, takes about two hours on 8 threads.)
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ def sha(a: np.ndarray) -> str:
     return oracle.sha256(np.ascontiguousarray(a).tobytes())
 
 
-def run(name: str, cfg: dict, steps: int, model=None, start: int = 1, log=None):
+def run(name: str, cfg: dict, steps: int, model=None, start: int = 1, log=None, log_micro=False):
     m = model or oracle.Model(cfg, I.init_params(cfg))
     recs = []
     for s in range(start, start + steps):
@@ -41,6 +42,8 @@ def run(name: str, cfg: dict, steps: int, model=None, start: int = 1, log=None):
             x, y = I.batch_for(name if name != "c2" else "c0", cfg, s, mb)
             losses.append(m.forward(x, y))
             m.backward()
+            if log and log_micro:
+                log(f"{name} step {s} micro-batch {mb} loss {float(losses[-1]):.6f} {time.time() - t0:.1f}s")
         grad = sha(m.grad)
         lr = I.lr_at(name if name != "c2" else "c0", s)
         m.adamw(lr)
@@ -79,6 +82,10 @@ def main():
             cfg = I.make_config("c3")
             _, recs = run("c3", cfg, 3, log=print)
             out = dict(config="c3", cfg=cfg, init_seed=I.INIT_SEED, steps=recs)
+        elif name == "c4":
+            cfg = I.make_config("c4")
+            _, recs = run("c4", cfg, 1, log=lambda t: print(t, flush=True), log_micro=True)
+            out = dict(config="c4", cfg=cfg, init_seed=I.INIT_SEED, steps=recs)
         else:
             raise SystemExit(f"unknown config {name}")
         out["oracle_threads"] = a.threads

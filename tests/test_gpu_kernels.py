@@ -70,9 +70,19 @@ def test_mfma_is_an_ascending_fma_chain(mlb, variant):
 
 
 # ------------------------------------------------------------------ exp / log
-@pytest.mark.parametrize("which", [0, 1, 2])
+# signed zeros, infinities, NaNs, the exp range ends and their neighbours, the
+# edges of the normal and subnormal scale ranges of exp, subnormals
+SPECIAL = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7FA00001,
+                    0x42B17217, 0x42B17218, 0x42B17219, 0xC2CFF1B4, 0xC2CFF1B5, 0xC2CFF1B6, 0x42AE0000, 0x42B00000,
+                    0xC2AE0000, 0xC2B00000, 0xC2B20000, 0xC2C80000, 0x00000001, 0x007FFFFF, 0x00800000,
+                    0x3F800000, 0xBF800000, 0x3F317218, 0xBF317218], dtype=np.uint32)
+
+
+@pytest.mark.parametrize("which", [0, 1, 2, 3])
 def test_elementary_spellings_match_oracle(mlb, which):
-    u = np.arange(0, 1 << 32, 257, dtype=np.uint64).astype(np.uint32)
+    """Every 257th bit pattern and the special inputs; spelling 3 is exp in
+    its branch-free form and must give exp's bits."""
+    u = np.concatenate([np.arange(0, 1 << 32, 257, dtype=np.uint64).astype(np.uint32), SPECIAL])
     x = u.view(np.float32)
     y = empty(x.size)
     mlb.unary(dev(x), y, x.size, which)
@@ -80,8 +90,8 @@ def test_elementary_spellings_match_oracle(mlb, which):
         want = np.empty_like(x)
         oracle.lib().orc_sigmoid_array(x, want, x.size)
     else:
-        want = (oracle.exp, oracle.log)[which](x)
-    assert_bits(["exp", "log", "sigmoid"][which], host(y), want)
+        want = (oracle.exp, oracle.log, None, oracle.exp)[which](x)
+    assert_bits(["exp", "log", "sigmoid", "exp (branch-free)"][which], host(y), want)
 
 
 # --------------------------------------------------------------- contractions
@@ -325,11 +335,24 @@ def test_swiglu(mlb):
     assert_bits("dgu", host(dgu).reshape(rows, 2 * F), dguo)
 
 
-@pytest.mark.parametrize("N,V", [(64, 256), (37, 50257)])
+# (64, 256) and (3, 25344) take the three-pass kernel; the others the
+# register-resident one: its smallest and largest row lengths, one where the
+# later waves hold only padding, and the 50,257-token vocabulary
+@pytest.mark.parametrize("N,V", [(64, 256), (3, 25344), (3, 25345), (8, 30000), (37, 50257), (5, 50688)])
 def test_cross_entropy(mlb, N, V):
     rng = np.random.default_rng(V)
     logits = (make(rng, (N, V)) * 4).astype(np.float32)
     tg = rng.integers(0, V, N).astype(np.int32)
+    # targets at both ends; a row whose maximum is -0 ahead of +0 (the sign of
+    # a zero maximum), one with -inf entries and the maximum last, one constant
+    tg[0], tg[1] = 0, V - 1
+    logits[0] = -np.abs(logits[0])
+    logits[0, 7], logits[0, V - 2] = np.float32(-0.0), np.float32(0.0)
+    if N > 2:
+        logits[2, ::3] = -np.inf
+        logits[2, V - 1] = np.float32(9.0)
+    if N > 3:
+        logits[3] = np.float32(0.25)
     rows, dl, loss = empty(N), empty(N * V), empty(1)
     mlb.cross_entropy(dev(logits), dev(tg), N, V, rows, dl, loss)
     lo, ro, dlo = oracle.cross_entropy(logits, tg)
