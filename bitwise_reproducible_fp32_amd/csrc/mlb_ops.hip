@@ -86,6 +86,82 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict_
     }
 }
 
+// Register-resident forms of the two row kernels above for rows of at most
+// 64 E entries: each lane loads its E entries (c = lane + 64 e) at once,
+// through range-checked buffer loads (entries past d read as 0, stores past d
+// are dropped), instead of walking the row twice. Same expressions and chain
+// order: forward, an entry past d adds fma(0, 0, acc) = acc (acc starts at +0
+// and is never -0); backward, entries past d are left out by a select.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* p, int64_t d) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)(d * 4), 0x00020000);
+}
+__device__ __forceinline__ float row_load(__amdgpu_buffer_rsrc_t rs, uint32_t c) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, c * 4u, 0, 0));
+}
+__device__ __forceinline__ void row_store(__amdgpu_buffer_rsrc_t rs, uint32_t c, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, c * 4u, 0, 0);
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd_reg(const float* __restrict__ x, const float* __restrict__ w,
+                                                         int64_t rows, int64_t d, float eps, float* __restrict__ y,
+                                                         float* __restrict__ r) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * d, d), rw = row_rsrc(w, d), ry = row_rsrc(y + row * d, d);
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = row_load(rx, lane + 64u * e);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = __builtin_fmaf(v[e], v[e], acc);
+    const float ss = wave_tree_sum(acc);
+    const float ms = ss / (float)d;
+    const float rr = 1.0f / __builtin_sqrtf(ms + eps);
+    if (lane == 0) r[row] = rr;
+#pragma unroll
+    for (int e = 0; e < E; ++e) row_store(ry, lane + 64u * e, (v[e] * rr) * row_load(rw, lane + 64u * e));
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx_reg(const float* __restrict__ dy, const float* __restrict__ x,
+                                                            const float* __restrict__ w, const float* __restrict__ r,
+                                                            int64_t rows, int64_t d, const float* base, float* out) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float rr = r[row];
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * d, d), rd = row_rsrc(dy + row * d, d), rw = row_rsrc(w, d);
+    float xh[E], gw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        xh[e] = row_load(rx, lane + 64u * e);
+        gw[e] = row_load(rd, lane + 64u * e);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        xh[e] = xh[e] * rr;
+        gw[e] = gw[e] * row_load(rw, lane + 64u * e);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = (int64_t)(lane + 64u * e) < d ? __builtin_fmaf(gw[e], xh[e], acc) : acc;
+    const float cc = wave_tree_sum(acc) / (float)d;
+    const __amdgpu_buffer_rsrc_t ro = row_rsrc(out + row * d, d);
+    if (base) {
+        const __amdgpu_buffer_rsrc_t rb = row_rsrc(base + row * d, d);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float dx = rr * (gw[e] - (xh[e] * cc));
+            row_store(ro, lane + 64u * e, row_load(rb, lane + 64u * e) + dx);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) row_store(ro, lane + 64u * e, rr * (gw[e] - (xh[e] * cc)));
+    }
+}
+
 // Per-chunk column partials of the gain gradient: for column c and chunk ch
 // (rows [1024 ch, 1024 ch + 1024)), part[ch][c] is an fma chain from +0 over
 // the chunk's rows in ascending order of dy[n][c] * (x[n][c] * r[n]). There
@@ -673,7 +749,11 @@ int rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float e
                 hipStream_t s) {
     if (rows < 0 || d <= 0) return -1;
     if (rows == 0) return 0;
-    k_rmsnorm_fwd<<<blocks(rows, 4), 256, 0, s>>>(x, w, rows, d, eps, y, r);
+    const unsigned g = blocks(rows, 4);
+    if (d <= 64 * 6) k_rmsnorm_fwd_reg<6><<<g, 256, 0, s>>>(x, w, rows, d, eps, y, r);
+    else if (d <= 64 * 12) k_rmsnorm_fwd_reg<12><<<g, 256, 0, s>>>(x, w, rows, d, eps, y, r);
+    else if (d <= 64 * 16) k_rmsnorm_fwd_reg<16><<<g, 256, 0, s>>>(x, w, rows, d, eps, y, r);
+    else k_rmsnorm_fwd<<<g, 256, 0, s>>>(x, w, rows, d, eps, y, r);
     return ok();
 }
 
@@ -681,7 +761,11 @@ int rmsnorm_bwd_dx(const float* dy, const float* x, const float* w, const float*
                    const float* base, float* out, hipStream_t s) {
     if (rows < 0 || d <= 0) return -1;
     if (rows == 0) return 0;
-    k_rmsnorm_bwd_dx<<<blocks(rows, 4), 256, 0, s>>>(dy, x, w, r, rows, d, base, out);
+    const unsigned g = blocks(rows, 4);
+    if (d <= 64 * 6) k_rmsnorm_bwd_dx_reg<6><<<g, 256, 0, s>>>(dy, x, w, r, rows, d, base, out);
+    else if (d <= 64 * 12) k_rmsnorm_bwd_dx_reg<12><<<g, 256, 0, s>>>(dy, x, w, r, rows, d, base, out);
+    else if (d <= 64 * 16) k_rmsnorm_bwd_dx_reg<16><<<g, 256, 0, s>>>(dy, x, w, r, rows, d, base, out);
+    else k_rmsnorm_bwd_dx<<<g, 256, 0, s>>>(dy, x, w, r, rows, d, base, out);
     return ok();
 }
 
