@@ -436,9 +436,10 @@ void k_gemm(KArgs a) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) { x0[e] = x0[e] * a.scale; x1[e] = x1[e] * a.scale; }
         }
-        // rotary embedding: this wave's 64 columns are one head, and the lane
-        // holds column i of it in x0 and column i + 32 in x1
-        if (WN == 2 && a.rope_cos && !a.split && j0 + 64 * wn < a.rope_cols) {
+        // rotary embedding (128-row tiles without a causal range): this
+        // wave's 64 columns (starting at a multiple of 64) are one head, and
+        // the lane holds column i of it in x0 and column i + 32 in x1
+        if (KR == 0 && MT == 128 && a.rope_cos && !a.split && j0 + 64 * wn < a.rope_cols) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t t = row(e) % a.rope_T;
@@ -634,6 +635,20 @@ bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Expected time, in units of one 128x128 workgroup's time at full residency,
+// of a grid of `wgs` workgroups that each cost `per_wg` of that. The chip
+// holds 768 of these workgroups at once (256 CUs x 3, for 128x128 and 128x64
+// tiles alike), so the grid runs in full waves of 768 plus a last partial
+// wave whose workgroups share their CU with fewer others and finish sooner:
+// 0.45 of a wave's time when at most 256 remain (one per CU), 0.75 up to 512.
+// The constants (and the 0.55 of a 128x64 tile) fit the measured times of the
+// step's contraction shapes; bits never depend on the choice.
+double grid_cost(int64_t wgs, double per_wg) {
+    const int64_t full = wgs / 768, tail = wgs % 768;
+    const double last = tail == 0 ? 0.0 : tail <= 256 ? 0.45 : tail <= 512 ? 0.75 : 1.0;
+    return per_wg * ((double)full + last);
+}
+
 }  // namespace
 
 static bool desc_ok(const GemmDesc& d) {
@@ -746,17 +761,18 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     vec = vec && (d.a_kc ? up4(d.K) <= d.lda : up4(d.M) <= d.lda) && (d.b_kc ? up4(d.K) <= d.ldb : up4(d.N) <= d.ldb);
     const bool rope = d.rope_cos != nullptr;
     if (rope && (!d.rope_sin || d.rope_T <= 0 || d.rope_cols % 64 != 0 || d.rope_cols > d.N || d.mode != 0 ||
-                 d.krange != 0 || d.outmask || d.batch != 1 || p.simple || p.tile > 0 || p.split == 1))
+                 d.krange != 0 || d.outmask || d.batch != 1 || p.simple || p.tile == 1 || p.split == 1))
         return -1;
     const bool split = !rope && want_split(d, p);
-    // 128x128 tiles in general; 128x64 when 128x128 tiles would not fill the
-    // chip once (fewer workgroups than 256 CUs x 3 resident); 256x64 for
-    // 64-wide outputs; 128x64 for causal ranges (their work per row tile grows
-    // along the diagonal)
-    int cfg = rope ? 0 : p.tile;
+    // Tiles: 128x64 for causal ranges (their work per row tile grows along
+    // the diagonal) and 256x64 for 64-wide outputs; otherwise 128x128 or
+    // 128x64, whichever grid is expected to finish first (grid_cost).
+    int cfg = p.tile;
     if (cfg < 0) {
-        const int64_t wg128 = ((d.M + 127) / 128) * ((d.N + 127) / 128) * (split ? nchunks(d) : 1) * d.batch;
-        cfg = d.krange != 0 ? 2 : (d.N <= 64 ? 1 : (wg128 < 768 ? 2 : 0));
+        const int64_t per = (split ? nchunks(d) : 1) * d.batch;
+        const int64_t wg128 = ((d.M + 127) / 128) * ((d.N + 127) / 128) * per;
+        const int64_t wg64 = ((d.M + 127) / 128) * ((d.N + 63) / 64) * per;
+        cfg = d.krange != 0 ? 2 : (d.N <= 64 && !rope ? 1 : (grid_cost(wg64, 0.55) < grid_cost(wg128, 1.0) ? 2 : 0));
     }
     int64_t nsplit = 1;
     if (split) {
