@@ -77,6 +77,8 @@ _SIGS = {
     "mlb_profile_version": (C.c_uint32, []),
     "mlb_prim_gemm": (i32, [i64, i64, i64, i64, vp, i64, i32, vp, i64, i32, vp, i64, i32, i32, i32, f32,
                             i64, i64, i64, i64, i64, i64, i64, i64, i32, i32, i32, vp, sz, vp]),
+    "mlb_prim_gemm_pair": (i32, [i64, i64, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                 i32, i32, i32, vp, sz, vp]),
     "mlb_prim_rmsnorm_fwd": (i32, [vp, vp, i64, i64, f32, vp, vp, vp]),
     "mlb_prim_rmsnorm_bwd": (i32, [vp, vp, vp, vp, i64, i64, vp, vp, vp, sz, vp]),
     "mlb_prim_rope": (i32, [vp, i64, i64, i64, i64, i64, f32, i32, vp]),
@@ -302,6 +304,15 @@ def gemm(A, B, C_, M, N, K, lda, a_kc, ldb, b_kc, ldc, kseg=0, krange=0, outmask
     check(lib().mlb_prim_gemm(M, N, K, kseg, _ptr(A), lda, int(a_kc), _ptr(B), ldb, int(b_kc), _ptr(C_), ldc,
                               krange, outmask, mode, float(scale), batch, heads, sA[0], sA[1], sB[0], sB[1],
                               sC[0], sC[1], tile, split, simple, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def gemm_pair(p0, p1, K, a_kc, b_kc, mode=0, ws=None, stream=None):
+    """p0, p1: (A, lda, B, ldb, C, ldc, M, N) of two contractions over K with one layout."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    (A0, lda0, B0, ldb0, C0, ldc0, M0, N0), (A1, lda1, B1, ldb1, C1, ldc1, M1, N1) = p0, p1
+    check(lib().mlb_prim_gemm_pair(M0, N0, M1, N1, K, _ptr(A0), lda0, _ptr(B0), ldb0, _ptr(C0), ldc0, _ptr(A1), lda1,
+                                   _ptr(B1), ldb1, _ptr(C1), ldc1, int(a_kc), int(b_kc), mode, _ptr(ws), ws_bytes,
+                                   _stream(stream)))
 
 
 def rmsnorm_fwd(x, w, eps, y, r, stream=None):

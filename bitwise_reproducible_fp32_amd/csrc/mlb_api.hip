@@ -194,13 +194,15 @@ int64_t split_floats(const Sizes& s) {
                                  {s.d, s.F, s.N, s.N},     {s.V, s.d, s.N, s.N},    {s.N, s.d, s.V, s.V},
                                  {s.N, s.d, s.F, s.F},     {s.N, s.d, 2 * s.F, s.F}, {s.N, s.d, 3 * s.d, s.d},
                                  {s.N, s.F, s.d, s.d},     {s.N, s.d, s.d, s.d}};
-    for (const auto& sh : shapes) {
+    int64_t f[11];
+    for (int i = 0; i < 11; ++i) {
         mlb::GemmDesc g;
-        g.M = sh[0]; g.N = sh[1]; g.K = sh[2]; g.kseg = sh[3];
-        int64_t f = mlb::gemm_split_scratch(g, auto_plan);
-        if (f > best) best = f;
+        g.M = shapes[i][0]; g.N = shapes[i][1]; g.K = shapes[i][2]; g.kseg = shapes[i][3];
+        f[i] = mlb::gemm_split_scratch(g, auto_plan);
+        if (f[i] > best) best = f[i];
     }
-    return best;
+    // the q/k/v and Wo weight gradients run as one launch (gemm_pair)
+    return best > f[0] + f[1] ? best : f[0] + f[1];
 }
 
 }  // namespace
@@ -506,6 +508,20 @@ mlb_status run_gemm(mlb_model* M, const char* site, const mlb::GemmDesc& g) {
         if (st_ != MLB_OK) return st_;               \
     } while (0)
 
+// Two independent contractions in one launch where they fit (mlb::gemm_pair).
+mlb_status run_gemm_pair(mlb_model* M, const char* site, const mlb::GemmDesc& g0, const mlb::GemmDesc& g1) {
+    mlb::GemmPlan p;
+    p.scratch = (M->overlap && M->cur == M->side) ? M->split_side : M->split;
+    p.scratch_floats = M->split_n;
+    GemmStatCtx ctx{M, site, -1};
+    mlb::LaunchTrace tr;
+    tr.ctx = &ctx; tr.begin = gemm_stat_begin; tr.end = gemm_stat_end;
+    const int r = mlb::gemm_pair(g0, g1, p, M->cur, M->stats_on ? &tr : nullptr);
+    if (r != 0) return fail(MLB_E_DEVICE, "contraction pair %ldx%ld and %ldx%ld failed (%d)", (long)g0.M, (long)g0.N,
+                            (long)g1.M, (long)g1.N, r);
+    return MLB_OK;
+}
+
 // A row or elementwise kernel with its algorithmic HBM bytes.
 #define OP(site, bytes, x)                                                           \
     do {                                                                             \
@@ -711,12 +727,8 @@ mlb_status backward(mlb_model* M) {
         float* dh1 = DH.buf[kh1];
         OP("rmsnorm_dx", f4 * (4 * N * d + N + d),
            mlb::rmsnorm_bwd_dx(DXN.buf[kx2], M->hmid[l], M->p + M->o_w2[l], M->r2[l], N, d, dh0, dh1, st));
-        // attention branch
+        // attention branch (its Wo weight gradient runs with the q/k/v one below)
         RUN("wo_dx", lin(N, d, d, dh1, d, true, M->p + M->o_wo[l], d, false, M->dO, d, 0));
-        CHK(to_side());
-        RUN("wo_dw", lin(d, d, N, dh1, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
-        CHK(ring_read(M, DH, kh1));
-        on_main();
         OP("attn_rowdot", f4 * (2 * N * d + BH * T), mlb::attn_rowdot(M->dO, M->O[l], s.B, H, T, hd, d, M->Dv, st));
         CHK(ring_claim(M, DQKV, kq));
         float* dqkv = DQKV.buf[kq];
@@ -752,9 +764,18 @@ mlb_status backward(mlb_model* M) {
         OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
         if (!dk_rope)
             OP("rope_bwd", f4 * 2 * N * d, mlb::rope(dqkv + d, s.B, T, H, hd, 3 * d, M->cosv, M->sinv, 1, st));
+        // the q/k/v and Wo weight gradients, one launch: the Wo grid fills the
+        // part-filled last wave of the q/k/v grid (disjoint parts of G, so the
+        // launch order does not matter to the bits)
         CHK(to_side());
-        RUN("qkv_dw", lin(3 * d, d, N, dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1));
+        {
+            const mlb_status st_ = run_gemm_pair(
+                M, "qkv_wo_dw", lin(3 * d, d, N, dqkv, 3 * d, false, M->xn1[l], d, false, M->G + M->o_qkv[l], d, 1),
+                lin(d, d, N, dh1, d, false, M->O[l], d, false, M->G + M->o_wo[l], d, 1));
+            if (st_ != MLB_OK) return st_;
+        }
         CHK(ring_read(M, DQKV, kq));
+        CHK(ring_read(M, DH, kh1));
         on_main();
         CHK(ring_claim(M, DXN, kx1));
         mlb::GemmDesc x1 = lin(N, d, 3 * d, dqkv, 3 * d, true, M->p + M->o_qkv[l], d, false, DXN.buf[kx1], d, 0);
@@ -1339,6 +1360,32 @@ mlb_status mlb_prim_gemm(int64_t M, int64_t N, int64_t K, int64_t kseg, const fl
     const int r = mlb::gemm(g, p, static_cast<hipStream_t>(stream));
     if (r == -1) return fail(MLB_E_INVALID_ARG, "invalid contraction description");
     if (r != 0) return fail(MLB_E_DEVICE, "contraction launch failed (%d)", r);
+    return MLB_OK;
+}
+
+mlb_status mlb_prim_gemm_pair(int64_t M0, int64_t N0, int64_t M1, int64_t N1, int64_t K, const float* A0,
+                              int64_t lda0, const float* B0, int64_t ldb0, float* C0, int64_t ldc0, const float* A1,
+                              int64_t lda1, const float* B1, int64_t ldb1, float* C1, int64_t ldc1, int a_kc, int b_kc,
+                              int mode, void* ws, size_t ws_bytes, void* stream) {
+    if (mode < 0 || mode > 1) return fail(MLB_E_INVALID_ARG, "mode %d", mode);
+    mlb::GemmDesc g[2];
+    const int64_t Ms[2] = {M0, M1}, Ns[2] = {N0, N1}, lda[2] = {lda0, lda1}, ldb[2] = {ldb0, ldb1},
+                  ldc[2] = {ldc0, ldc1};
+    const float* As[2] = {A0, A1};
+    const float* Bs[2] = {B0, B1};
+    float* Cs[2] = {C0, C1};
+    for (int i = 0; i < 2; ++i) {
+        g[i].M = Ms[i]; g[i].N = Ns[i]; g[i].K = K; g[i].kseg = K;
+        g[i].A = As[i]; g[i].lda = lda[i]; g[i].a_kc = a_kc != 0;
+        g[i].B = Bs[i]; g[i].ldb = ldb[i]; g[i].b_kc = b_kc != 0;
+        g[i].C = Cs[i]; g[i].ldc = ldc[i]; g[i].mode = mode;
+    }
+    mlb::GemmPlan p;
+    p.scratch = static_cast<float*>(ws);
+    p.scratch_floats = (int64_t)(ws_bytes / 4);
+    const int r = mlb::gemm_pair(g[0], g[1], p, static_cast<hipStream_t>(stream));
+    if (r == -1) return fail(MLB_E_INVALID_ARG, "invalid contraction description");
+    if (r != 0) return fail(MLB_E_DEVICE, "contraction pair launch failed (%d)", r);
     return MLB_OK;
 }
 

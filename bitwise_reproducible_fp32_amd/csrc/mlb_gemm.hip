@@ -49,6 +49,9 @@ struct KArgs {
     float scale;
     float* part;
     int64_t tiles_m, tiles_n, ntiles;
+    // this problem's share of the grid: ntiles x nsplit x batch workgroups,
+    // numbered after those of the problems before it in the same launch
+    int64_t nsplit, nwg;
     // chunk >= 0: this launch runs only that 1024-chunk of a causal contraction
     // over row tiles tm_lo.. (launched in chunk order; rows whose first chunk
     // it is store, later chunks add to C)
@@ -79,9 +82,12 @@ __device__ __forceinline__ void epilogue_store(const KArgs& a, int mode, float* 
 template <bool VEC, bool MC>
 constexpr int gemm_waves_per_eu() { return (VEC && !MC) ? 3 : 1; }
 
+// One launch runs one contraction, or two independent ones of the same kind
+// (a0 first, then a1; a1.nwg == 0 when there is one): the second fills the
+// part-filled last wave of the first.
 template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, bool VEC, bool MC, int KT, bool ABLK = false>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(gemm_waves_per_eu<VEC, MC>())))
-void k_gemm(KArgs a) {
+void k_gemm(KArgs a0, KArgs a1) {
     // Each wave owns RB 32-row blocks x 64 columns (two 32x32 MFMA blocks per
     // row block). MC: the contraction may span several 1024-chunks, so a
     // running total is kept beside the chunk accumulator.
@@ -101,11 +107,15 @@ void k_gemm(KArgs a) {
     const int wm = wave % WM, wn = wave / WM;
     const int lk = lane >> 5, li = lane & 31;
 
-    // XCD-aware order over (tile, chunk, problem), problem slowest, then
-    // grouped tile rows inside a problem.
-    const int64_t lb = xcd_logical_block();
-    const int64_t gy = (lb / gridDim.x) % gridDim.y, gz = lb / ((int64_t)gridDim.x * gridDim.y);
-    const int64_t logical = lb % gridDim.x;
+    // XCD-aware order over (tile, chunk, batch problem), batch slowest, then
+    // grouped tile rows inside a problem; the launch's first contraction
+    // takes the first a0.nwg logical workgroups.
+    int64_t lb = xcd_logical_block();
+    const bool second = lb >= a0.nwg;
+    const KArgs& a = second ? a1 : a0;
+    if (second) lb -= a0.nwg;
+    const int64_t gy = (lb / a.ntiles) % a.nsplit, gz = lb / (a.ntiles * a.nsplit);
+    const int64_t logical = lb % a.ntiles;
     constexpr int64_t GM = 8;
     const int64_t per_group = GM * a.tiles_n;
     const int64_t first_m = (logical / per_group) * GM;
@@ -566,16 +576,16 @@ struct Cfg { int wm, wn; };
 thread_local char g_launched[96];
 
 template <bool AKC, bool BKC, int WM, int WN, int RB, int KR, int KT = 32, bool ABLK = false>
-void launch_t(const KArgs& a, bool vec, bool mc, dim3 grid, hipStream_t s) {
+void launch_t(const KArgs& a, const KArgs& b, bool vec, bool mc, dim3 grid, hipStream_t s) {
     std::snprintf(g_launched, sizeof g_launched, "k_gemm<%s, %s, %d, %d, %d, %d, %s, %s, %d, %s>",
                   AKC ? "true" : "false", BKC ? "true" : "false", WM, WN, RB, KR, vec ? "true" : "false",
                   mc ? "true" : "false", KT, ABLK ? "true" : "false");
     if (mc) {
-        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
-        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a, b);
+        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, true, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a, b);
     } else {
-        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
-        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a);
+        if (vec) k_gemm<AKC, BKC, WM, WN, RB, KR, true, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a, b);
+        else k_gemm<AKC, BKC, WM, WN, RB, KR, false, false, KT, ABLK><<<grid, 64 * WM * WN, 0, s>>>(a, b);
     }
 }
 
@@ -585,49 +595,57 @@ void launch_t(const KArgs& a, bool vec, bool mc, dim3 grid, hipStream_t s) {
 // tm_count >= 0 restricts the launch to row tiles [tm_lo, tm_lo + tm_count).
 int64_t tile_rows(int cfg) { return cfg == 1 ? 256 : 128; }
 
-bool launch_tiled(const GemmDesc& d, KArgs a, int cfg, bool vec, bool mc, int64_t nsplit, hipStream_t s,
-                  int64_t tm_lo = 0, int64_t tm_count = -1) {
+// The grid of one problem in tile configuration cfg: ntiles x nsplit x batch
+// workgroups. tm_count >= 0 restricts it to row tiles [tm_lo, tm_lo + tm_count).
+void set_grid(KArgs& a, const GemmDesc& d, int cfg, int64_t nsplit, int64_t tm_lo = 0, int64_t tm_count = -1) {
     const int64_t MT = tile_rows(cfg), NT = cfg == 0 ? 128 : 64;
     a.tm_lo = tm_lo;
     a.tiles_m = tm_count >= 0 ? tm_count : (d.M + MT - 1) / MT;
     a.tiles_n = (d.N + NT - 1) / NT;
     a.ntiles = a.tiles_m * a.tiles_n;
-    const dim3 grid((unsigned)a.ntiles, (unsigned)nsplit, (unsigned)d.batch);
+    a.nsplit = nsplit;
+    a.nwg = a.ntiles * nsplit * d.batch;
+}
+
+// Launches a (gridded by set_grid), followed in the same grid by b when
+// b.nwg > 0 (same layout, tile configuration and variant).
+bool launch_tiled(const GemmDesc& d, const KArgs& a, const KArgs& b, int cfg, bool vec, bool mc, hipStream_t s) {
+    const dim3 grid((unsigned)(a.nwg + b.nwg));
     const int key = (d.a_kc ? 1 : 0) | (d.b_kc ? 2 : 0);
     if (d.krange == 0 && cfg == 0) {
         switch (key) {
-            case 3: launch_t<true, true, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
-            case 1: launch_t<true, false, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
-            case 0: launch_t<false, false, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
-            case 2: launch_t<false, true, 2, 2, 2, 0>(a, vec, mc, grid, s); return true;
+            case 3: launch_t<true, true, 2, 2, 2, 0>(a, b, vec, mc, grid, s); return true;
+            case 1: launch_t<true, false, 2, 2, 2, 0>(a, b, vec, mc, grid, s); return true;
+            case 0: launch_t<false, false, 2, 2, 2, 0>(a, b, vec, mc, grid, s); return true;
+            case 2: launch_t<false, true, 2, 2, 2, 0>(a, b, vec, mc, grid, s); return true;
         }
     }
     if (d.krange == 0 && cfg == 1) {
         switch (key) {
-            case 3: launch_t<true, true, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
-            case 1: launch_t<true, false, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
-            case 0: launch_t<false, false, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
-            case 2: launch_t<false, true, 4, 1, 2, 0>(a, vec, mc, grid, s); return true;
+            case 3: launch_t<true, true, 4, 1, 2, 0>(a, b, vec, mc, grid, s); return true;
+            case 1: launch_t<true, false, 4, 1, 2, 0>(a, b, vec, mc, grid, s); return true;
+            case 0: launch_t<false, false, 4, 1, 2, 0>(a, b, vec, mc, grid, s); return true;
+            case 2: launch_t<false, true, 4, 1, 2, 0>(a, b, vec, mc, grid, s); return true;
         }
     }
     if (d.krange == 0 && cfg == 2) {
         switch (key) {
-            case 3: launch_t<true, true, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
-            case 1: launch_t<true, false, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
-            case 0: launch_t<false, false, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
-            case 2: launch_t<false, true, 4, 1, 1, 0>(a, vec, mc, grid, s); return true;
+            case 3: launch_t<true, true, 4, 1, 1, 0>(a, b, vec, mc, grid, s); return true;
+            case 1: launch_t<true, false, 4, 1, 1, 0>(a, b, vec, mc, grid, s); return true;
+            case 0: launch_t<false, false, 4, 1, 1, 0>(a, b, vec, mc, grid, s); return true;
+            case 2: launch_t<false, true, 4, 1, 1, 0>(a, b, vec, mc, grid, s); return true;
         }
     }
     // causal ranges; a tiled A (32x32 blocks, the attention probability layout)
     // is read as whole contiguous 4 KiB tiles
     if (d.krange == 1 && key == 1 && cfg == 2) {
-        if (d.a_blk) launch_t<true, false, 4, 1, 1, 1, 32, true>(a, vec, mc, grid, s);
-        else launch_t<true, false, 4, 1, 1, 1, 32>(a, vec, mc, grid, s);
+        if (d.a_blk) launch_t<true, false, 4, 1, 1, 1, 32, true>(a, b, vec, mc, grid, s);
+        else launch_t<true, false, 4, 1, 1, 1, 32>(a, b, vec, mc, grid, s);
         return true;
     }
     if (d.krange == 2 && key == 0 && cfg == 2) {
-        if (d.a_blk) launch_t<false, false, 4, 1, 1, 2, 32, true>(a, vec, mc, grid, s);
-        else launch_t<false, false, 4, 1, 1, 2, 32>(a, vec, mc, grid, s);
+        if (d.a_blk) launch_t<false, false, 4, 1, 1, 2, 32, true>(a, b, vec, mc, grid, s);
+        else launch_t<false, false, 4, 1, 1, 2, 32>(a, b, vec, mc, grid, s);
         return true;
     }
     return false;
@@ -720,11 +738,8 @@ struct Traced {
 };
 }  // namespace
 
-int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace* tr) {
-    std::snprintf(g_launched, sizeof g_launched, "none");
-    const Traced t{tr};
-    if (!desc_ok(d)) return -1;
-    if (d.M == 0 || d.N == 0) return 0;
+namespace {
+KArgs make_args(const GemmDesc& d) {
     KArgs a{};
     a.M = d.M; a.N = d.N; a.K = d.K; a.kseg = d.K > 0 ? d.kseg : 1;
     a.A = d.A; a.lda = d.lda; a.B = d.B; a.ldb = d.ldb; a.C = d.C; a.ldc = d.ldc; a.R = d.R;
@@ -732,6 +747,36 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     a.outmask = d.outmask; a.mode = d.mode; a.krange = d.krange; a.scale = d.scale;
     a.split = 0; a.part = nullptr; a.chunk = -1; a.tm_lo = 0;
     a.rope_cos = d.rope_cos; a.rope_sin = d.rope_sin; a.rope_T = d.rope_T; a.rope_cols = d.rope_cols;
+    return a;
+}
+
+// float4 loads need 16-byte alignment and a leading dimension that covers
+// the contiguous extent rounded up to 4 (the slack is read, then masked)
+bool vec_loads(const GemmDesc& d) {
+    auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
+    const bool v = aligned16(d.A) && aligned16(d.B) && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
+                   d.sAb % 4 == 0 && d.sAh % 4 == 0 && d.sBb % 4 == 0 && d.sBh % 4 == 0;
+    return v && (d.a_kc ? up4(d.K) <= d.lda : up4(d.M) <= d.lda) && (d.b_kc ? up4(d.K) <= d.ldb : up4(d.N) <= d.ldb);
+}
+
+// The split partials of a (already written) added in chunk order, then the
+// epilogue mode: the second kernel of the split path.
+void launch_fold(const GemmDesc& d, const KArgs& a, hipStream_t s) {
+    const int64_t n = d.M * d.N;
+    const bool v4 = d.N % 4 == 0 && d.ldc % 4 == 0 && aligned16(d.C) && aligned16(a.part) &&
+                    (d.mode != 3 || aligned16(d.R));
+    if (v4) k_fold4<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(a.part, a.nsplit, d.M, d.N, a);
+    else k_fold<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.part, a.nsplit, d.M, d.N, a);
+}
+}  // namespace
+
+int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace* tr) {
+    std::snprintf(g_launched, sizeof g_launched, "none");
+    const Traced t{tr};
+    if (!desc_ok(d)) return -1;
+    if (d.M == 0 || d.N == 0) return 0;
+    KArgs a = make_args(d);
+    KArgs none{};   // no second problem in the launch
     // The causal attention contractions of 64-wide heads (tiled P, square,
     // one segment) have their own kernel when the plan leaves the choice open.
     if (p.tile < 0 && p.split < 0 && !p.simple && d.a_blk && d.mode == 0 && !d.outmask && !d.b_kc &&
@@ -753,12 +798,7 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
         t.end(gemm_flops(d, 0, d.K), 0.0);
         return hipGetLastError() == hipSuccess ? 0 : -3;
     }
-    // float4 loads need 16-byte alignment and a leading dimension that covers
-    // the contiguous extent rounded up to 4 (the slack is read, then masked)
-    auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
-    bool vec = aligned16(d.A) && aligned16(d.B) && d.lda % 4 == 0 && d.ldb % 4 == 0 &&
-               d.sAb % 4 == 0 && d.sAh % 4 == 0 && d.sBb % 4 == 0 && d.sBh % 4 == 0;
-    vec = vec && (d.a_kc ? up4(d.K) <= d.lda : up4(d.M) <= d.lda) && (d.b_kc ? up4(d.K) <= d.ldb : up4(d.N) <= d.ldb);
+    const bool vec = vec_loads(d);
     const bool rope = d.rope_cos != nullptr;
     if (rope && (!d.rope_sin || d.rope_T <= 0 || d.rope_cols % 64 != 0 || d.rope_cols > d.N || d.mode != 0 ||
                  d.krange != 0 || d.outmask || d.batch != 1 || p.simple || p.tile == 1 || p.split == 1))
@@ -796,8 +836,9 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
             else { lo = 0; const int64_t e = (c + 1) * KC < d.M ? (c + 1) * KC : d.M; hi = (e + MT - 1) / MT; }
             if (lo >= hi) continue;
             a.chunk = c;
+            set_grid(a, d, cfg, 1, lo, hi - lo);
             t.begin();
-            if (!launch_tiled(d, a, cfg, vec, false, 1, s, lo, hi - lo)) return -1;
+            if (!launch_tiled(d, a, none, cfg, vec, false, s)) return -1;
             t.end(gemm_flops(d, c * KC, (c + 1) * KC), 0.0);
             if (hipGetLastError() != hipSuccess) return -3;
         }
@@ -805,8 +846,9 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
     }
     // several chunks (or segments) per workgroup need the running total
     const bool mc = !split && nch > 1;
+    set_grid(a, d, cfg, nsplit);
     t.begin();
-    if (!launch_tiled(d, a, cfg, vec, mc, nsplit, s)) {
+    if (!launch_tiled(d, a, none, cfg, vec, mc, s)) {
         if (split || rope) return -1;
         const int64_t n = d.M * d.N;
         const dim3 grid((unsigned)((n + 255) / 256), 1, (unsigned)d.batch);
@@ -823,14 +865,63 @@ int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace*
         std::memcpy(main_kernel, g_launched, sizeof g_launched);
         std::snprintf(g_launched, sizeof g_launched, "k_fold");
         t.begin();
-        const bool v4 = d.N % 4 == 0 && d.ldc % 4 == 0 && aligned16(d.C) && aligned16(p.scratch) &&
-                        (d.mode != 3 || aligned16(d.R));
-        if (v4) k_fold4<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(p.scratch, nsplit, d.M, d.N, a);
-        else k_fold<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(p.scratch, nsplit, d.M, d.N, a);
+        launch_fold(d, a, s);
         // partials read, output written (and read when accumulating)
         t.end(0.0, 4.0 * (double)n * (double)(nsplit + 1 + (d.mode == 1 || d.mode == 3 ? 1 : 0)));
         std::memcpy(g_launched, main_kernel, sizeof g_launched);
         if (hipGetLastError() != hipSuccess) return -3;
+    }
+    return 0;
+}
+
+int gemm_pair(const GemmDesc& d0, const GemmDesc& d1, const GemmPlan& p, hipStream_t s, const LaunchTrace* tr) {
+    std::snprintf(g_launched, sizeof g_launched, "none");
+    const Traced t{tr};
+    if (!desc_ok(d0) || !desc_ok(d1)) return -1;
+    // Only plain contractions of one layout and load width pair up, under the
+    // automatic plan, both split into per-chunk partials or both one chunk.
+    auto plain = [](const GemmDesc& d) {
+        return d.M > 0 && d.N > 64 && d.K > 0 && d.krange == 0 && !d.outmask && d.batch == 1 && !d.rope_cos &&
+               !d.a_blk;
+    };
+    const bool s0 = want_split(d0, p), s1 = want_split(d1, p);
+    const int64_t n0 = nchunks(d0), n1 = nchunks(d1);
+    const int64_t part0 = s0 ? n0 * d0.M * d0.N : 0, part1 = s1 ? n1 * d1.M * d1.N : 0;
+    const bool same = plain(d0) && plain(d1) && d0.a_kc == d1.a_kc && d0.b_kc == d1.b_kc &&
+                      vec_loads(d0) == vec_loads(d1) && p.tile < 0 && p.split < 0 && !p.simple &&
+                      ((s0 && s1 && p.scratch && p.scratch_floats >= part0 + part1) || (n0 == 1 && n1 == 1));
+    if (!same) {
+        const int r = gemm(d0, p, s, tr);
+        return r != 0 ? r : gemm(d1, p, s, tr);
+    }
+    KArgs a = make_args(d0), b = make_args(d1);
+    const int64_t c0 = s0 ? n0 : 1, c1 = s1 ? n1 : 1;
+    auto wg = [](const GemmDesc& d, int64_t nt, int64_t c) { return ((d.M + 127) / 128) * ((d.N + nt - 1) / nt) * c; };
+    const int cfg = grid_cost(wg(d0, 64, c0) + wg(d1, 64, c1), 0.55) < grid_cost(wg(d0, 128, c0) + wg(d1, 128, c1), 1.0)
+                        ? 2 : 0;
+    if (s0) {
+        a.split = 1; a.part = p.scratch;
+        b.split = 1; b.part = p.scratch + part0;
+    }
+    set_grid(a, d0, cfg, c0);
+    set_grid(b, d1, cfg, c1);
+    t.begin();
+    if (!launch_tiled(d0, a, b, cfg, vec_loads(d0), false, s)) return -1;
+    t.end(gemm_flops(d0, 0, d0.K) + gemm_flops(d1, 0, d1.K), 0.0);
+    if (hipGetLastError() != hipSuccess) return -3;
+    if (s0) {
+        char main_kernel[sizeof g_launched];
+        std::memcpy(main_kernel, g_launched, sizeof g_launched);
+        std::snprintf(g_launched, sizeof g_launched, "k_fold");
+        for (int i = 0; i < 2; ++i) {
+            const GemmDesc& d = i ? d1 : d0;
+            const KArgs& k = i ? b : a;
+            t.begin();
+            launch_fold(d, k, s);
+            t.end(0.0, 4.0 * (double)(d.M * d.N) * (double)(k.nsplit + 1 + (d.mode == 1 || d.mode == 3 ? 1 : 0)));
+            if (hipGetLastError() != hipSuccess) return -3;
+        }
+        std::memcpy(g_launched, main_kernel, sizeof g_launched);
     }
     return 0;
 }

@@ -34,8 +34,8 @@ struct GemmDesc {
     // Rotary embedding in the epilogue (mode 0, 64-wide heads): output columns
     // [0, rope_cols) are heads of 64 whose pairs (i, i + 32) at position
     // t = row mod rope_T are rotated by cos/sin[t][i] exactly as the rope
-    // kernel does. Forces 128x128 tiles (a wave's 64 columns are one head, and
-    // a lane holds both elements of its pairs) and no split.
+    // kernel does. Needs 128-row tiles (128x128 or 128x64: a wave's 64 columns
+    // are one head, and a lane holds both elements of its pairs) and no split.
     const float* rope_cos = nullptr;
     const float* rope_sin = nullptr;
     int64_t rope_T = 0, rope_cols = 0;
@@ -74,6 +74,14 @@ int64_t gemm_split_scratch(const GemmDesc& d, const GemmPlan& p);
 // tr (may be null) sees every dispatch: the contraction launches (one, or one
 // per chunk of a causal range) and the split path's k_fold.
 int gemm(const GemmDesc& d, const GemmPlan& p, hipStream_t s, const LaunchTrace* tr = nullptr);
+// Two independent contractions: in one launch (one grid, d0's workgroups
+// first, then d1's, the second filling the first's part-filled last wave)
+// when both are plain (no causal range, mask, batch or rotary epilogue) and
+// share the layout, load width and split choice under the automatic plan;
+// otherwise one after the other. With split partials, d1's follow d0's in the
+// plan's scratch. Bits equal those of two gemm() calls.
+int gemm_pair(const GemmDesc& d0, const GemmDesc& d1, const GemmPlan& p, hipStream_t s,
+              const LaunchTrace* tr = nullptr);
 // FLOPs of the valid multiply-adds of d with k in [kb, ke), all problems.
 double gemm_flops(const GemmDesc& d, int64_t kb, int64_t ke);
 // Name of the contraction kernel the last gemm() call on this thread launched.

@@ -40,6 +40,19 @@ mlb_status mlb_prim_gemm(int64_t M, int64_t N, int64_t K, int64_t kseg, const fl
                          int64_t sBb, int64_t sBh, int64_t sCb, int64_t sCh, int tile, int split, int simple,
                          void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Two independent contractions of one kind in one launch, as the training
+ * step runs the q/k/v and Wo weight gradients: problem 0 (M0 x N0) and problem
+ * 1 (M1 x N1), both over K (one segment), both with the layout a_kc/b_kc and
+ * mode (0 store, 1 accumulate) of mlb_prim_gemm, under its automatic plan. When
+ * they cannot share a launch (a causal range, a mask, 64-wide outputs, other
+ * load widths) they run one after the other; the bits are the same either way.
+ * ws: the per-chunk partials of both (ceil(K/1024)*(M0*N0 + M1*N1) floats)
+ * when K > 1024; too small a ws makes them run unsplit. */
+mlb_status mlb_prim_gemm_pair(int64_t M0, int64_t N0, int64_t M1, int64_t N1, int64_t K, const float* A0,
+                              int64_t lda0, const float* B0, int64_t ldb0, float* C0, int64_t ldc0, const float* A1,
+                              int64_t lda1, const float* B1, int64_t ldb1, float* C1, int64_t ldc1, int a_kc, int b_kc,
+                              int mode, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* RMSNorm over rows of d (model card: RMSNorm eps 1e-6, pre-norm):
  * r = 1/sqrt(DOT64(x,x)/d + eps), y = (x*r)*w. x,y [rows,d], r [rows]. */
 mlb_status mlb_prim_rmsnorm_fwd(const float* x, const float* w, int64_t rows, int64_t d, float eps, float* y,

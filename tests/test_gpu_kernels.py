@@ -223,6 +223,33 @@ def test_sweep_weight_gradient_shape(mlb):
         assert_bits(f"dW split {split}", host(C).reshape(o, i)[rows], want)
 
 
+@pytest.mark.parametrize("M0,N0,M1,N1,K,layout", [(2304, 768, 768, 768, 2048, "tn"), (300, 100, 129, 260, 3000, "tn"),
+                                                   (200, 132, 70, 96, 700, "nn"), (130, 97, 64, 200, 1500, "nt")])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_contraction_pair(mlb, M0, N0, M1, N1, K, layout, mode):
+    """Two contractions in one launch (as the step runs the q/k/v and Wo weight
+    gradients): each gets its own oracle bits, with split partials or one
+    chunk, on ragged tiles and odd widths; without a workspace the two run one
+    after the other with running totals, with the same bits."""
+    rng = np.random.default_rng(M0 + N1 + K)
+    a_kc, b_kc = layout[0] == "n", layout[1] == "t"
+    probs = []
+    for M, N in ((M0, N0), (M1, N1)):
+        A = make(rng, (M, K) if a_kc else (K, M))
+        B = make(rng, (N, K) if b_kc else (K, N))
+        C0 = make(rng, (M, N))
+        lda, ldb = (K if a_kc else M), (K if b_kc else N)
+        want = orc_contract(A, B, M, N, K, lda, a_kc, ldb, b_kc, mode=mode, C0=C0 if mode else None)
+        probs.append((A, lda, B, ldb, C0, M, N, want))
+    nch = (K + 1023) // 1024
+    for ws in (empty(nch * (M0 * N0 + M1 * N1)), None):
+        outs = [dev(C0.copy()) for (_, _, _, _, C0, _, _, _) in probs]
+        args = [(dev(A), lda, dev(B), ldb, C, N, M, N) for (A, lda, B, ldb, _, M, N, _), C in zip(probs, outs)]
+        mlb.gemm_pair(args[0], args[1], K, a_kc, b_kc, mode=mode, ws=ws)
+        for i, ((_, _, _, _, _, M, N, want), C) in enumerate(zip(probs, outs)):
+            assert_bits(f"pair problem {i} ws {ws is not None}", host(C).reshape(M, N), want)
+
+
 # ------------------------------------------------------------- row operations
 @pytest.mark.parametrize("rows,d", [(8192, 767), (8192, 768), (3, 32)])
 def test_rmsnorm(mlb, rows, d):
