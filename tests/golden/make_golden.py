@@ -3,7 +3,7 @@
 Every value here comes from the CPU oracle (oracle/), run on the seeded inputs
 of bitwise_reproducible_fp32_amd.inputs; nothing is taken from the HIP path.
 Usage: python tests/golden/make_golden.py c0 c2 c3 c4 [--threads N]
-(c4, one full step of the 162M decoder, takes about two hours on 8 threads.)
+(c4, one full step of the 162M decoder, takes about three hours on 8 threads.)
 """
 from __future__ import annotations
 
