@@ -96,9 +96,16 @@ _SIGS = {
 
 
 def lib():
-    """The loaded HIP library. Raises if it has not been built: there is no fallback."""
+    """The loaded HIP library. Raises if it has not been built: there is no fallback.
+
+    PyTorch is imported first: its wheel carries its own HIP runtime, which the
+    library must share (both are named libamdhip64.so.7 to the dynamic loader,
+    which reuses whichever copy is loaded first). Loading the library first
+    would bring in a second runtime for PyTorch, and device memory and streams
+    of one would be invalid in the other."""
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (the HIP runtime the library links against)
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with bitwise_reproducible_fp32_amd/build.py "
                               "(or __graft_entry__.build()); there is no CPU fallback")

@@ -4,6 +4,8 @@ here touches a GPU."""
 import ctypes as C
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -31,6 +33,7 @@ def declared_symbols():
 
 
 def test_every_declared_symbol_is_exported(mlb):
+    mlb.lib()   # PyTorch's HIP runtime first (see test_one_hip_runtime_in_the_process)
     lib = C.CDLL(mlb.LIB_PATH)
     syms = declared_symbols()
     assert len(syms) >= 25
@@ -88,3 +91,16 @@ def test_null_arguments_refused(mlb):
     n = C.c_size_t()
     assert L.mlb_save(None, None, 0, C.byref(n)) == -1
     assert L.mlb_destroy(None) == 0
+
+
+def test_one_hip_runtime_in_the_process(mlb):
+    """The binding loads PyTorch's HIP runtime before the library, so a process
+    holds one copy of it. PyTorch's wheel carries its own, under the same
+    soname; loaded second, it would be a second runtime in which the library's
+    device pointers and streams are invalid."""
+    code = ("import bitwise_reproducible_fp32_amd as m; m.lib(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=600)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1", r.stdout

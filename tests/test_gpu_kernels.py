@@ -250,6 +250,47 @@ def test_contraction_pair(mlb, M0, N0, M1, N1, K, layout, mode):
             assert_bits(f"pair problem {i} ws {ws is not None}", host(C).reshape(M, N), want)
 
 
+def test_empty_and_degenerate_sizes(mlb):
+    """An empty contraction (K = 0) is +0 (mode 0) or C + (+0) (mode 1, so a
+    -0 in C becomes +0); M = 0 or N = 0 writes nothing; zero rows of RMSNorm,
+    SwiGLU, AdamW and the scatter leave their outputs as they were, and the
+    RMSNorm gain gradient over zero rows is the empty contraction, +0."""
+    L = mlb.lib()
+    st = mlb._stream()
+    p = mlb._ptr
+    M, N = 5, 7
+    C0 = np.array([-0.0, 1.5, -2.25, 0.0, 3.0, -1.0, 7.5] * M, np.float32)
+    A, B = dev(np.ones(64, np.float32)), dev(np.ones(64, np.float32))
+    for mode in (0, 1):
+        C = dev(C0.copy())
+        mlb.gemm(A, B, C, M, N, 0, 4, True, 4, True, N, mode=mode)
+        want = np.zeros_like(C0) if mode == 0 else C0 + np.float32(0.0)
+        assert_bits(f"K = 0 mode {mode}", host(C), want)
+    for m_, n_ in ((0, N), (M, 0)):
+        C = dev(C0.copy())
+        mlb.gemm(A, B, C, m_, n_, 3, 4, True, 4, True, N)
+        assert_bits(f"M {m_} N {n_} untouched", host(C), C0)
+    sentinel = np.full(64, 7.0, np.float32)
+    x, w, y, r, dx, dw, ws = (dev(sentinel.copy()) for _ in range(7))
+    mlb.check(L.mlb_prim_rmsnorm_fwd(p(x), p(w), 0, 8, 1e-6, p(y), p(r), st))
+    mlb.check(L.mlb_prim_rmsnorm_bwd(p(x), p(x), p(w), p(r), 0, 8, p(dx), p(dw), p(ws), 256, st))
+    assert_bits("rmsnorm y", host(y), sentinel)
+    assert_bits("rmsnorm r", host(r), sentinel)
+    assert_bits("rmsnorm dx", host(dx), sentinel)
+    assert_bits("rmsnorm dw over no rows", host(dw)[:8], np.zeros(8, np.float32))
+    a = dev(sentinel.copy())
+    mlb.check(L.mlb_prim_swiglu_fwd(p(x), 0, 8, p(a), st))
+    assert_bits("swiglu a", host(a), sentinel)
+    pp, g, m, v = (dev(sentinel.copy()) for _ in range(4))
+    mlb.check(L.mlb_prim_adamw(p(pp), p(g), p(m), p(v), 0, 1e-3, 0.9, 0.95, 1e-8, 0.1, 1, st))
+    for name, t in (("p", pp), ("g", g), ("m", m), ("v", v)):
+        assert_bits(f"adamw {name}", host(t), sentinel)
+    ids = dev(np.zeros(8, np.int32))
+    dE = dev(sentinel.copy())
+    mlb.embed_scatter(ids, x, 0, 8, 8, dE, empty(2 * 8192 * 2))
+    assert_bits("scatter dE", host(dE), sentinel)
+
+
 # ------------------------------------------------------------- row operations
 @pytest.mark.parametrize("rows,d", [(8192, 767), (8192, 768), (3, 32)])
 def test_rmsnorm(mlb, rows, d):
@@ -291,7 +332,8 @@ def test_rope(mlb):
 # register-resident softmax.
 @pytest.mark.parametrize("BH,T,hd,tiled", [(2, 64, 8, 0), (2, 64, 8, 1), (3, 300, 5, 0), (2, 1100, 64, 0),
                                            (2, 1088, 64, 1), (3, 96, 5, 1), (1, 2080, 64, 1), (2, 64, 64, 1),
-                                           (3, 192, 64, 1), (2, 1024, 64, 1), (1, 2048, 64, 1), (2, 601, 8, 0)])
+                                           (3, 192, 64, 1), (2, 1024, 64, 1), (1, 2048, 64, 1), (2, 601, 8, 0),
+                                           (3, 1, 5, 0), (2, 1, 64, 0)])
 def test_attention_fwd_bwd(mlb, BH, T, hd, tiled):
     rng = np.random.default_rng(T + hd)
     q, k, v, dO = (make(rng, (BH, T, hd)) for _ in range(4))
