@@ -142,8 +142,9 @@ def main() -> int:
                          "known traffic that scales the HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; the data-parallel path over several "
-                                   "GPUs is a design (DESIGN.md), not implemented", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "the step runs on exactly one GPU; the data-parallel path over several "
+                                   "GPUs (a fixed-order hand-off of the shard gradients) is not implemented",
+                          "n_gpus": a.gpus}))
         return 2
 
     import torch

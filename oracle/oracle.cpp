@@ -12,7 +12,7 @@
 // "What bitwise identity means": reduction order, partitioning, FMA policy,
 // flush seams, transcendental spellings and tie rules are all fixed). The
 // pages print none of the concrete rules, so the profile below (MLB-P1) is
-// this build's reading; every rule is restated where it is used.
+// the reading adopted here; every rule is restated where it is used.
 //
 // Arithmetic environment: IEEE binary32, round-to-nearest-even, gradual
 // underflow (no FTZ/DAZ), no contraction (built with -ffp-contract=off), no

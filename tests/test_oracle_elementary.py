@@ -1,6 +1,6 @@
 """Pins of the oracle's exp/log spellings and of its arithmetic environment.
 
-exp_p and log_p are this build's own spellings (Cody-Waite reduction with a
+exp_p and log_p are the profile's own spellings (Cody-Waite reduction with a
 Taylor polynomial; atanh series), so the pins are mathematical: closeness to
 binary64 exp/log, exact special values, the overflow/underflow thresholds,
 monotonicity, and the absence of flush-to-zero."""
