@@ -283,7 +283,7 @@ class Model:
         return out
 
     def set_overlap(self, on: bool) -> None:
-        """Backward weight-gradient work on the library's second stream (default on)."""
+        """Backward weight-gradient work on the library's second stream (default off)."""
         check(lib().mlb_set_overlap(self.h, int(bool(on))))
 
     def stats_enable(self, on: bool = True) -> None:

@@ -234,7 +234,7 @@ struct mlb_model {
     hipStream_t stream;        // the caller's stream: every call is ordered on it
     hipStream_t side = nullptr;
     hipStream_t cur = nullptr; // the stream the op being enqueued runs on
-    bool overlap = true;       // backward weight-gradient work on the side stream
+    bool overlap = false;      // backward weight-gradient work on the side stream (off: one stream is faster)
     std::vector<hipEvent_t> sync_pool;
     size_t sync_next = 0;
     int device;

@@ -170,7 +170,7 @@ mlb_status mlb_stage_card(const mlb_model* m, int stage, int layer, mlb_card* ou
 /* Card of a state array (params, accumulated gradient, AdamW moments). */
 mlb_status mlb_state_card(const mlb_model* m, mlb_which which, mlb_card* out);
 
-/* Stream overlap of the backward pass (default on). When on, the work that
+/* Stream overlap of the backward pass (default off). When on, the work that
  * only feeds the gradient accumulator (weight-gradient contractions, norm-gain
  * gradients, the embedding scatter) runs on a library-owned second stream of
  * default priority, concurrently with the input-gradient chain on the caller's
