@@ -323,19 +323,47 @@ __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int6
     }
 }
 
-// D_i = DOT64 over the head dimension of dO and O, one wavefront per row.
+// D_i = DOT64 over the head dimension of dO and O. A wavefront takes
+// ROWDOT_R consecutive rows (z, i) and, for heads of at most 64, loads all of
+// them before the first chain, so that more loads are in flight per wave; each
+// row is still its own lane chain and tree.
+constexpr int ROWDOT_R = 4;
 __global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, const float* __restrict__ O,
                                                 int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
                                                 float* __restrict__ D) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWDOT_R;
     const int lane = threadIdx.x & 63;
-    if (row >= B * H * T) return;
-    const int64_t i = row % T, z = row / T, b = z / H, h = z % H;
-    const int64_t off = (b * T + i) * ld + h * hd;
-    float acc = 0.0f;
-    for (int64_t c = lane; c < hd; c += 64) acc = __builtin_fmaf(dO[off + c], O[off + c], acc);
-    const float t = wave_tree_sum(acc);
-    if (lane == 0) D[row] = t;
+    const int64_t nrows = B * H * T;
+    if (row0 >= nrows) return;
+    auto offset = [&](int64_t row) -> int64_t {
+        const int64_t i = row % T, z = row / T, b = z / H, h = z % H;
+        return (b * T + i) * ld + h * hd;
+    };
+    if (hd <= 64) {
+        float x[ROWDOT_R], y[ROWDOT_R];
+#pragma unroll
+        for (int k = 0; k < ROWDOT_R; ++k) {
+            const int64_t row = row0 + k;
+            const bool in = row < nrows && lane < hd;
+            const int64_t off = in ? offset(row) + lane : 0;
+            x[k] = in ? dO[off] : 0.0f;
+            y[k] = in ? O[off] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < ROWDOT_R; ++k) {
+            // a lane past hd holds no element: its chain stays +0 (fma(0, 0, +0) is +0)
+            const float t = wave_tree_sum(__builtin_fmaf(x[k], y[k], 0.0f));
+            if (lane == 0 && row0 + k < nrows) D[row0 + k] = t;
+        }
+        return;
+    }
+    for (int k = 0; k < ROWDOT_R && row0 + k < nrows; ++k) {
+        const int64_t off = offset(row0 + k);
+        float acc = 0.0f;
+        for (int64_t c = lane; c < hd; c += 64) acc = __builtin_fmaf(dO[off + c], O[off + c], acc);
+        const float t = wave_tree_sum(acc);
+        if (lane == 0) D[row0 + k] = t;
+    }
 }
 
 // dS = (P * (dP - D_i)) * scale over j <= i, written over dP.
@@ -578,7 +606,17 @@ __global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ x
 __global__ __launch_bounds__(64) void k_sum64(const float* __restrict__ v, int64_t n, float mul, float* out) {
     const int lane = threadIdx.x;
     float acc = 0.0f;
-    for (int64_t i = lane; i < n; i += 64) acc = acc + v[i];
+    // the lane's elements i = lane + 64 m in ascending m, 16 loads in flight
+    // ahead of their additions
+    constexpr int U = 16;
+    for (int64_t i0 = lane; i0 < n; i0 += 64 * U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = i0 + 64 * u < n ? v[i0 + 64 * u] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + 64 * u < n) acc = acc + x[u];
+    }
     const float t = wave_tree_sum(acc);
     if (lane == 0) out[0] = t * mul;
 }
@@ -803,7 +841,7 @@ int softmax_causal(float* P, int64_t nbh, int64_t T, int blk, hipStream_t s) {
 int attn_rowdot(const float* dO, const float* O, int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
                 float* D, hipStream_t s) {
     if (B * H * T == 0) return 0;
-    k_rowdot<<<blocks(B * H * T, 4), 256, 0, s>>>(dO, O, B, H, T, hd, ld, D);
+    k_rowdot<<<blocks(B * H * T, 4 * ROWDOT_R), 256, 0, s>>>(dO, O, B, H, T, hd, ld, D);
     return ok();
 }
 
