@@ -329,11 +329,12 @@ def test_rope(mlb):
 # hd = 64 with T a multiple of 64 and tiled P runs the paired-row-tile
 # kernel (single tile, odd tile count, one and two 1024-chunks); the other
 # shapes run the general contraction. T = 601 is an odd row count for the
-# register-resident softmax.
+# register-resident softmax; T = 2048 with 5-wide heads is the sweep's causal
+# softmax at full length.
 @pytest.mark.parametrize("BH,T,hd,tiled", [(2, 64, 8, 0), (2, 64, 8, 1), (3, 300, 5, 0), (2, 1100, 64, 0),
                                            (2, 1088, 64, 1), (3, 96, 5, 1), (1, 2080, 64, 1), (2, 64, 64, 1),
                                            (3, 192, 64, 1), (2, 1024, 64, 1), (1, 2048, 64, 1), (2, 601, 8, 0),
-                                           (3, 1, 5, 0), (2, 1, 64, 0)])
+                                           (3, 1, 5, 0), (2, 1, 64, 0), (2, 2048, 5, 1), (1, 2048, 5, 0)])
 def test_attention_fwd_bwd(mlb, BH, T, hd, tiled):
     rng = np.random.default_rng(T + hd)
     q, k, v, dO = (make(rng, (BH, T, hd)) for _ in range(4))
