@@ -387,9 +387,10 @@ def test_attention_strided_heads(mlb):
                 assert_bits(f"{name} b{b} h{h}", dg[b, :, i, h], want[i][0])
 
 
-def test_swiglu(mlb):
-    rng = np.random.default_rng(3)
-    rows, F = 4096, 1024
+@pytest.mark.parametrize("rows,F", [(4096, 1024), (37, 1023), (5, 6)])
+def test_swiglu(mlb, rows, F):
+    """float4 path (F % 4 == 0) and the one-element path."""
+    rng = np.random.default_rng(3 + F)
     gu = (make(rng, (rows, 2 * F)) * 8).astype(np.float32)
     dA = make(rng, (rows, F))
     a = empty(rows * F)
