@@ -259,6 +259,40 @@ __global__ __launch_bounds__(256) void k_rope(float* x, int64_t B, int64_t T, in
     }
 }
 
+// The same rotation on four adjacent pairs per thread (hd/2 % 4 == 0, 16-byte
+// aligned rows and tables, fewer than 2^31 pairs in all and in a row's
+// stride): float4 traffic and 32-bit index arithmetic, the same operations
+// per element.
+__global__ __launch_bounds__(256) void k_rope4(float* x, uint32_t npairs4, uint32_t T, uint32_t H, uint32_t hd,
+                                               uint32_t ld, const float* __restrict__ cosv,
+                                               const float* __restrict__ sinv, int backward) {
+    const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= npairs4) return;
+    const uint32_t h2 = hd / 2, idx = 4u * q;
+    const uint32_t i = idx % h2, h = (idx / h2) % H, n = idx / (h2 * H);
+    const uint32_t t = n % T;
+    float* row = x + (size_t)n * ld + (size_t)h * hd;
+    const float4 c4 = *reinterpret_cast<const float4*>(cosv + (size_t)t * h2 + i);
+    const float4 s4 = *reinterpret_cast<const float4*>(sinv + (size_t)t * h2 + i);
+    const float4 a4 = *reinterpret_cast<const float4*>(row + i);
+    const float4 b4 = *reinterpret_cast<const float4*>(row + i + h2);
+    const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float x0[4] = {a4.x, a4.y, a4.z, a4.w}, x1[4] = {b4.x, b4.y, b4.z, b4.w};
+    float r0[4], r1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (!backward) {
+            r0[e] = (x0[e] * cs[e]) - (x1[e] * sn[e]);
+            r1[e] = (x1[e] * cs[e]) + (x0[e] * sn[e]);
+        } else {
+            r0[e] = (x0[e] * cs[e]) + (x1[e] * sn[e]);
+            r1[e] = (x1[e] * cs[e]) - (x0[e] * sn[e]);
+        }
+    }
+    *reinterpret_cast<float4*>(row + i) = make_float4(r0[0], r0[1], r0[2], r0[3]);
+    *reinterpret_cast<float4*>(row + i + h2) = make_float4(r1[0], r1[1], r1[2], r1[3]);
+}
+
 // Causal softmax in place, one wavefront per row i over j <= i:
 // m = MAX64, e = exp(S - m), Z = SUM64(e), P = e * (1 / Z).
 __global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t T, int blk) {
@@ -865,7 +899,13 @@ int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, cons
     if (hd % 2 != 0 || B < 0 || T < 0 || H < 0) return -1;
     const int64_t n = B * T * H * (hd / 2);
     if (n == 0) return 0;
-    k_rope<<<blocks(n, 256), 256, 0, s>>>(x, B, T, H, hd, ld, cosv, sinv, backward);
+    const bool v4 = (hd / 2) % 4 == 0 && ld % 4 == 0 && hd % 4 == 0 && n < ((int64_t)1 << 31) &&
+                    B * T * ld < ((int64_t)1 << 31) && ((uintptr_t)x & 15u) == 0 && ((uintptr_t)cosv & 15u) == 0 &&
+                    ((uintptr_t)sinv & 15u) == 0;
+    if (v4)
+        k_rope4<<<blocks(n / 4, 256), 256, 0, s>>>(x, (uint32_t)(n / 4), (uint32_t)T, (uint32_t)H, (uint32_t)hd,
+                                                    (uint32_t)ld, cosv, sinv, backward);
+    else k_rope<<<blocks(n, 256), 256, 0, s>>>(x, B, T, H, hd, ld, cosv, sinv, backward);
     return ok();
 }
 

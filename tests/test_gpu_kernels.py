@@ -311,9 +311,10 @@ def test_rmsnorm(mlb, rows, d):
     assert_bits("dw", host(dw), dwo)
 
 
-def test_rope(mlb):
-    rng = np.random.default_rng(2)
-    B, T, H, hd = 2, 2048, 3, 64
+@pytest.mark.parametrize("B,T,H,hd", [(2, 2048, 3, 64), (1, 37, 2, 8), (1, 33, 2, 6)])
+def test_rope(mlb, B, T, H, hd):
+    """Four pairs per thread (hd / 2 a multiple of 4) and one pair per thread."""
+    rng = np.random.default_rng(2 + hd)
     ld = 3 * H * hd
     x = make(rng, (B * T, ld))
     c, s = oracle.rope_table(T, hd, 10000.0)
