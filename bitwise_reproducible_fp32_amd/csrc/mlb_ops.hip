@@ -293,6 +293,36 @@ __global__ __launch_bounds__(256) void k_rope4(float* x, uint32_t npairs4, uint3
     *reinterpret_cast<float4*>(row + i + h2) = make_float4(r1[0], r1[1], r1[2], r1[3]);
 }
 
+// exp_p without branches, bit for bit the same function: the reduction and
+// polynomial run on 0 in place of a NaN or out-of-range input and the special
+// result is selected at the end; the scale 2^k is applied as (p * s1) * s2
+// with s2 = 1 in the normal range, where multiplying by 1 is exact. For code
+// that evaluates many exponentials per thread, where the branches of exp_p
+// would each hold an exec mask.
+__device__ __forceinline__ float exp_p_select(float x) {
+    const bool nan = x != x, hi = x >= u2f(0x42B17218u), lo = x <= u2f(0xC2CFF1B5u);
+    const float xs = (nan || hi || lo) ? 0.0f : x;
+    const float shifter = 12582912.0f;
+    const float t = xs * u2f(0x3FB8AA3Bu);
+    const float kf = (t + shifter) - shifter;
+    const int ki = (int)kf;
+    float r = __builtin_fmaf(-kf, u2f(0x3F317200u), xs);
+    r = __builtin_fmaf(-kf, u2f(0x35BFBE8Eu), r);
+    float p = u2f(0x39500D01u);
+    p = __builtin_fmaf(p, r, u2f(0x3AB60B61u));
+    p = __builtin_fmaf(p, r, u2f(0x3C088889u));
+    p = __builtin_fmaf(p, r, u2f(0x3D2AAAABu));
+    p = __builtin_fmaf(p, r, u2f(0x3E2AAAABu));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const bool big = ki > 127, small = ki < -126;
+    const float s1 = big ? u2f(0x7F000000u) : u2f((uint32_t)(small ? ki + 253 : ki + 127) << 23);
+    const float s2 = big ? 2.0f : (small ? u2f(0x00800000u) : 1.0f);
+    const float v = (p * s1) * s2;
+    return nan ? x : (hi ? __builtin_inff() : (lo ? 0.0f : v));
+}
+
 // Causal softmax in place, one wavefront per row i over j <= i:
 // m = MAX64, e = exp(S - m), Z = SUM64(e), P = e * (1 / Z).
 __global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t T, int blk) {
@@ -345,7 +375,7 @@ __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int6
 #pragma unroll
     for (int m = 0; m < PER; ++m)
         if (lane + 64 * m < n) {
-            v[m] = exp_p(v[m] - mx);
+            v[m] = exp_p_select(v[m] - mx);
             acc = acc + v[m];
         }
     const float Z = wave_tree_sum(acc);
@@ -538,35 +568,6 @@ __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* 
     for (int64_t v = vfull; v < V; v += 64) o[v] = grad(v, l[v]);
 }
 
-// exp_p without branches, bit for bit the same function: the reduction and
-// polynomial run on 0 in place of a NaN or out-of-range input and the special
-// result is selected at the end; the scale 2^k is applied as (p * s1) * s2
-// with s2 = 1 in the normal range, where multiplying by 1 is exact. For code
-// that evaluates many exponentials per thread, where the branches of exp_p
-// would each hold an exec mask.
-__device__ __forceinline__ float exp_p_select(float x) {
-    const bool nan = x != x, hi = x >= u2f(0x42B17218u), lo = x <= u2f(0xC2CFF1B5u);
-    const float xs = (nan || hi || lo) ? 0.0f : x;
-    const float shifter = 12582912.0f;
-    const float t = xs * u2f(0x3FB8AA3Bu);
-    const float kf = (t + shifter) - shifter;
-    const int ki = (int)kf;
-    float r = __builtin_fmaf(-kf, u2f(0x3F317200u), xs);
-    r = __builtin_fmaf(-kf, u2f(0x35BFBE8Eu), r);
-    float p = u2f(0x39500D01u);
-    p = __builtin_fmaf(p, r, u2f(0x3AB60B61u));
-    p = __builtin_fmaf(p, r, u2f(0x3C088889u));
-    p = __builtin_fmaf(p, r, u2f(0x3D2AAAABu));
-    p = __builtin_fmaf(p, r, u2f(0x3E2AAAABu));
-    p = __builtin_fmaf(p, r, 0.5f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    const bool big = ki > 127, small = ki < -126;
-    const float s1 = big ? u2f(0x7F000000u) : u2f((uint32_t)(small ? ki + 253 : ki + 127) << 23);
-    const float s2 = big ? 2.0f : (small ? u2f(0x00800000u) : 1.0f);
-    const float v = (p * s1) * s2;
-    return nan ? x : (hi ? __builtin_inff() : (lo ? 0.0f : v));
-}
 
 // Cross-entropy of a long row read from HBM once: a workgroup of XR_W waves
 // owns one row, and thread (w, lane) holds v = lane + 64 (w C + c), c < C,
