@@ -275,7 +275,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded Zipf(1.1) token ids, N(0,0.02) init)",
+        "data": ("synthetic (seeded order-2 Markov bytes, N(0,0.02) init)" if a.config == "c0" else
+                 "synthetic (seeded Zipf(1.1) token ids, N(0,0.02) init)"),
         "config": {"workload": f"{a.config}: {I.param_count(cfg):,}-param decoder, {S} micro-batches of "
                                f"{B}x{T} tokens per step", "tokens_per_step": tokens, "micro_batches": S,
                    "batch": B, "seq_len": T, "parallelism": "none (1 GPU)", "stream_overlap": bool(a.overlap)},
