@@ -712,15 +712,17 @@ __global__ __launch_bounds__(1024) void k_sort_keys(const int32_t* __restrict__ 
         key[q] = k;
     }
     __syncthreads();
-    for (int64_t size = 2; size <= P; size <<= 1) {
-        for (int64_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int64_t q = threadIdx.x; q < P; q += blockDim.x) {
-                const int64_t partner = q ^ stride;
-                if (partner > q) {
-                    const bool up = (q & size) == 0;
-                    const uint64_t a = key[q], b = key[partner];
-                    if ((a > b) == up) { key[q] = b; key[partner] = a; }
-                }
+    // each thread takes whole compare-exchange pairs (q, q + stride): pair r
+    // has q = r with a 0 bit inserted at the stride's position
+    const int np = (int)P / 2;
+    for (int size = 2; size <= (int)P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const int ls = __builtin_ctz((unsigned)stride);
+            for (int r = (int)threadIdx.x; r < np; r += (int)blockDim.x) {
+                const int q = ((r >> ls) << (ls + 1)) | (r & (stride - 1)), partner = q | stride;
+                const bool up = (q & size) == 0;
+                const uint64_t a = key[q], b = key[partner];
+                if ((a > b) == up) { key[q] = b; key[partner] = a; }
             }
             __syncthreads();
         }
