@@ -460,7 +460,16 @@ void k_gemm(KArgs a0, KArgs a1) {
                 x1[e] = r1;
             }
         }
-        if (interior) {
+        if (interior && a.split) {
+            // split partials are read once, by the fold: nontemporal stores
+            // keep them from displacing the operand panels in the L2
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t gi = row(e);
+                __builtin_nontemporal_store(x0[e], out + gi * ld + gj0);
+                __builtin_nontemporal_store(x1[e], out + gi * ld + gj1);
+            }
+        } else if (interior) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t gi = row(e);
@@ -537,8 +546,9 @@ __global__ __launch_bounds__(256) void k_fold(const float* __restrict__ part, in
 }
 
 // The same fold for four adjacent outputs of a row per thread (N % 4 == 0,
-// 16-byte aligned partials and rows): float4 traffic, and the partials of up
-// to 8 chunks loaded before the first addition, which is still in chunk order.
+// 16-byte aligned partials and rows): float4 traffic, nontemporal loads (each
+// partial is read once), and the partials of up to 8 chunks loaded before the
+// first addition, which is still in chunk order.
 __global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, int64_t nch, int64_t M, int64_t N,
                                                KArgs a) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -546,12 +556,15 @@ __global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, i
     if (idx >= MN) return;
     const float4* p4 = reinterpret_cast<const float4*>(part);
     const int64_t MN4 = MN / 4;
-    float4 t = p4[q];
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f* pv = reinterpret_cast<const v4f*>(part);
+    const v4f t0 = __builtin_nontemporal_load(pv + q);
+    float4 t = make_float4(t0.x, t0.y, t0.z, t0.w);
     for (int64_t c0 = 1; c0 < nch; c0 += 8) {
-        float4 x[8];
+        v4f x[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-            if (c0 + u < nch) x[u] = p4[(c0 + u) * MN4 + q];
+            if (c0 + u < nch) x[u] = __builtin_nontemporal_load(pv + (c0 + u) * MN4 + q);
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             if (c0 + u < nch) { t.x = t.x + x[u].x; t.y = t.y + x[u].y; t.z = t.z + x[u].z; t.w = t.w + x[u].w; }
