@@ -21,8 +21,12 @@ CXXFLAGS = ["-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fno-fast-math", "-
 
 
 def build(compiler: str = "g++", out: str = LIB_PATH, extra: list[str] | None = None) -> str:
-    cmd = [compiler, *CXXFLAGS, *(extra or []), "-o", out, SRC]
+    """Compiles oracle.cpp; the new library replaces the old one by rename, so a
+    process that has the old one loaded keeps running on it."""
+    tmp = f"{out}.tmp{os.getpid()}"
+    cmd = [compiler, *CXXFLAGS, *(extra or []), "-o", tmp, SRC]
     subprocess.run(cmd, check=True, cwd=HERE)
+    os.replace(tmp, out)
     return out
 
 
@@ -144,7 +148,8 @@ def set_threads(n: int) -> None:
 
 SABOTAGE = {"gemm_reverse_k": 1, "gemm_kc512": 2, "gemm_pairwise_chunks": 3, "gemm_mul_add": 4,
             "w64_mirror_pairing": 5, "w32_lanes": 6, "libm_exp": 7, "ftz_daz": 8,
-            "softmax_divide": 9, "adamw_decoupled": 10, "scatter_reverse": 11, "libm_log": 12}
+            "softmax_divide": 9, "adamw_decoupled": 10, "scatter_reverse": 11, "libm_log": 12,
+            "rms_dw_unchunked": 13, "swiglu_bwd_spelling": 14, "ds_spelling": 15, "w64_blocks": 16}
 
 
 def set_sabotage(arm: int) -> None:
@@ -357,21 +362,6 @@ class Model:
         B, T = self.cfg["batch"], self.cfg["seq_len"]
         rows = logits.reshape(B, T, -1)[:, position, :]
         return np.array([argmax(r) for r in rows], np.int32)
-
-    def cards(self, state: bool = True) -> list:
-        """Identity cards of the oracle's stages and state arrays, in the same
-        order and byte layout as the library's (hashed with the oracle's own
-        SHA-256)."""
-        from bitwise_reproducible_fp32_amd.cards import Card, STATE_NAMES, card_order, stage_tag
-        out = []
-        for st, l in card_order(self.cfg["n_layers"]):
-            a = self.stage(st, l)
-            out.append(Card(stage_tag(st, l), "f32", int(a.size), sha256(np.ascontiguousarray(a).tobytes())))
-        if state:
-            for w, name in enumerate(STATE_NAMES):   # params, grad, adam_m, adam_v
-                a = self.read(w)
-                out.append(Card(name, "f32", int(a.size), sha256(a.tobytes())))
-        return out
 
     def stage(self, stage: int, layer: int = 0) -> np.ndarray:
         n = lib().orc_model_stage(self.h, stage, layer, None)

@@ -11,12 +11,28 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from bitwise_reproducible_fp32_amd.inputs import param_shapes
+
+def layout(cfg):
+    """(name, shape) of every parameter in checkpoint order, written out here
+    from the model definition: the input table [V, d]; per layer the attention
+    norm gain [d], Wq, Wk, Wv, Wo [d, d], the MLP norm gain [d], Wg, Wu [F, d],
+    Wd [d, F]; the output table [V, d] unless it is tied to the input table.
+    Linear weights are [out_features, in_features]."""
+    V, d, F = cfg["vocab"], cfg["d_model"], cfg["ffn_hidden"]
+    out = [("E_in", (V, d))]
+    for l in range(cfg["n_layers"]):
+        out.append((f"l{l}.attn_norm", (d,)))
+        out += [(f"l{l}.W{x}", (d, d)) for x in "qkvo"]
+        out.append((f"l{l}.mlp_norm", (d,)))
+        out += [(f"l{l}.Wg", (F, d)), (f"l{l}.Wu", (F, d)), (f"l{l}.Wd", (d, F))]
+    if not cfg["tied"]:
+        out.append(("W_out", (V, d)))
+    return out
 
 
 def unpack(cfg, flat):
     out, o = {}, 0
-    for name, shape, _ in param_shapes(cfg):
+    for name, shape in layout(cfg):
         n = int(np.prod(shape))
         out[name] = flat[o:o + n].reshape(shape)
         o += n

@@ -8,6 +8,7 @@ import pytest
 import oracle
 from bitwise_reproducible_fp32_amd import inputs as I
 from bitwise_reproducible_fp32_amd.cards import Card, card_order, first_divergence, stage_tag
+from oracle_cards import FINAL_STAGES, LAYER_STAGES, oracle_cards as cards_of
 
 
 def test_first_divergence_logic():
@@ -24,6 +25,12 @@ def test_card_order_follows_the_forward_pass():
     assert order[:4] == ["L0.h_in", "L0.r1", "L0.xn1", "L0.qkv"]
     assert order.index("L0.a") < order.index("L1.h_in")
     assert order[-3:] == ["h_L", "dlogits", "loss_rows"]
+    # the library's order and tags equal the test side's own literal list
+    literal = [f"L{l}.{n}" for l in range(2) for _, n in LAYER_STAGES] + [n for _, n in FINAL_STAGES]
+    assert order == literal
+    # and the library's stage ids name the same stages as the oracle's export
+    assert [s for s, l in card_order(2)] == [s for l in range(2) for s, _ in LAYER_STAGES] + \
+        [s for s, _ in FINAL_STAGES]
 
 
 def oracle_cards(arm: str | None):
@@ -34,7 +41,7 @@ def oracle_cards(arm: str | None):
         x, y = I.c0_batch(0, cfg["batch"], cfg["seq_len"])
         m.forward(x, y)
         m.backward()
-        return m.cards()
+        return cards_of(m)
     finally:
         oracle.set_sabotage(0)
 
@@ -53,4 +60,4 @@ def test_cards_are_deterministic(clean_cards):
 def test_planted_rule_change_is_located(clean_cards, arm, first):
     bad = oracle_cards(arm)
     d = first_divergence(clean_cards, bad)
-    assert d is not None and d.tag == first, (arm, d)
+    assert d is not None and d[0] == first, (arm, d)
