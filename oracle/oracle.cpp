@@ -41,7 +41,8 @@ int g_threads = 1;
 enum {
     SAB_NONE = 0, SAB_GEMM_REVERSE_K, SAB_GEMM_KC512, SAB_GEMM_PAIRWISE, SAB_GEMM_MULADD,
     SAB_W64_MIRROR, SAB_W32, SAB_LIBM_EXP, SAB_FTZ_DAZ, SAB_SOFTMAX_DIVIDE, SAB_ADAMW_DECOUPLED,
-    SAB_SCATTER_REVERSE, SAB_LIBM_LOG, SAB_COUNT
+    SAB_SCATTER_REVERSE, SAB_LIBM_LOG, SAB_RMS_DW_UNCHUNKED, SAB_SWIGLU_BWD_SPELLING,
+    SAB_DS_SPELLING, SAB_W64_BLOCKS, SAB_COUNT
 };
 int g_sab = SAB_NONE;
 
@@ -130,11 +131,17 @@ template <class Op> float tree(float* acc, Op op) {
 }
 inline float addf(float a, float b) { return a + b; }
 
+// Lane of element i of n (the sabotage arm deals contiguous blocks instead).
+inline int64_t lane_of(int64_t i, int64_t n, int W) {
+    if (g_sab == SAB_W64_BLOCKS) { const int64_t blk = (n + W - 1) / W; return i / blk; }
+    return i % W;
+}
+
 float sum64(const float* v, int64_t n) {
     float acc[64];
     const int W = lanes();
     for (int l = 0; l < 64; ++l) acc[l] = 0.0f;
-    for (int64_t i = 0; i < n; ++i) acc[i % W] = acc[i % W] + v[i];
+    for (int64_t i = 0; i < n; ++i) { const int64_t l = lane_of(i, n, W); acc[l] = acc[l] + v[i]; }
     return tree(acc, addf);
 }
 
@@ -142,7 +149,7 @@ float dot64(const float* a, const float* b, int64_t n) {
     float acc[64];
     const int W = lanes();
     for (int l = 0; l < 64; ++l) acc[l] = 0.0f;
-    for (int64_t i = 0; i < n; ++i) acc[i % W] = std::fma(a[i], b[i], acc[i % W]);
+    for (int64_t i = 0; i < n; ++i) { const int64_t l = lane_of(i, n, W); acc[l] = std::fma(a[i], b[i], acc[l]); }
     return tree(acc, addf);
 }
 
@@ -150,7 +157,7 @@ float max64(const float* v, int64_t n) {
     float acc[64];
     const int W = lanes();
     for (int l = 0; l < 64; ++l) acc[l] = -INFINITY;
-    for (int64_t i = 0; i < n; ++i) acc[i % W] = max_keep(acc[i % W], v[i]);
+    for (int64_t i = 0; i < n; ++i) { const int64_t l = lane_of(i, n, W); acc[l] = max_keep(acc[l], v[i]); }
     return tree(acc, max_keep);
 }
 
@@ -282,10 +289,12 @@ void rmsnorm_bwd(const float* dy, const float* x, const float* w, const float* r
         }
     }
     // gain gradient: per column, chunks of 1024 rows, fma chain from +0, left fold
+    // (the sabotage arm runs one chain over all rows)
     std::vector<float> acc((size_t)d), tot((size_t)d);
     bool have = false;
-    for (int64_t c0 = 0; c0 < rows; c0 += KC) {
-        const int64_t c1 = std::min<int64_t>(rows, c0 + KC);
+    const int64_t kc = (g_sab == SAB_RMS_DW_UNCHUNKED) ? std::max<int64_t>(rows, 1) : KC;
+    for (int64_t c0 = 0; c0 < rows; c0 += kc) {
+        const int64_t c1 = std::min<int64_t>(rows, c0 + kc);
         for (int64_t c = 0; c < d; ++c) acc[c] = 0.0f;
         for (int64_t n = c0; n < c1; ++n) {
             const float rr = r[n];
@@ -389,7 +398,9 @@ void attention_bwd(int64_t B, int64_t H, int64_t T, int64_t hd, const float* q, 
 #pragma omp parallel for num_threads(g_threads) schedule(static)
             for (int64_t i = 0; i < T; ++i)
                 for (int64_t j = 0; j <= i; ++j)
-                    dS[i * T + j] = (Pb[i * T + j] * (dS[i * T + j] - D[i])) * scale;
+                    dS[i * T + j] = (g_sab == SAB_DS_SPELLING)
+                                        ? ((Pb[i * T + j] * dS[i * T + j]) - (Pb[i * T + j] * D[i])) * scale
+                                        : (Pb[i * T + j] * (dS[i * T + j] - D[i])) * scale;
             Gemm gq{T, hd, T, T, dS.data(), T, 1, k + off, ld, 1, 0, 1.0f, 1, 0};
             gemm_run(gq, dq + off, ld);
             Gemm gk{T, hd, T, T, dS.data(), 1, T, q + off, ld, 1, 0, 1.0f, 2, 0};
@@ -420,7 +431,8 @@ void swiglu_bwd(const float* dA, int64_t ldda, const float* gu, int64_t rows, in
             const float da = dA[n * ldda + f];
             const float sg = sigmoid_p(g);
             const float silu = g * sg;
-            const float dsilu = sg * (1.0f + (g * (1.0f - sg)));
+            const float dsilu = (g_sab == SAB_SWIGLU_BWD_SPELLING) ? sg + (silu * (1.0f - sg))
+                                                                   : sg * (1.0f + (g * (1.0f - sg)));
             dgu[n * ldgu + F + f] = da * silu;
             dgu[n * ldgu + f] = (da * u) * dsilu;
         }

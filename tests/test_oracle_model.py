@@ -51,7 +51,7 @@ def test_matches_float64_reference(name, over):
     g = m.grad
     assert abs(float(loss) - l64) / abs(l64) <= 1e-5
     o = 0
-    for pname, shape, _ in I.param_shapes(cfg):
+    for pname, shape in ref64.layout(cfg):
         n = int(np.prod(shape))
         a, b = g[o:o + n].astype(np.float64), g64[o:o + n]
         assert np.linalg.norm(a - b) <= 1e-3 * np.linalg.norm(b), pname
@@ -232,7 +232,8 @@ def test_threads_do_not_change_model_bits():
 
 
 MODEL_ARMS = ["gemm_reverse_k", "gemm_mul_add", "w64_mirror_pairing", "w32_lanes", "libm_exp",
-              "softmax_divide", "adamw_decoupled", "scatter_reverse"]
+              "softmax_divide", "adamw_decoupled", "scatter_reverse", "w64_blocks", "swiglu_bwd_spelling",
+              "ds_spelling"]
 
 
 @pytest.mark.parametrize("arm", MODEL_ARMS)
