@@ -1187,6 +1187,8 @@ mlb_status mlb_read_stage(const mlb_model* M, int stage, int layer, void* dst, s
         case 11: src = M->h[s.L]; n = s.N * s.d; break;
         case 12: src = M->logits; n = s.N * s.V; break;   // rows compacted from the padded stride
         case 13: src = M->loss_rows; n = s.N; break;
+        case 14: src = M->cosv; n = s.T * (s.hd / 2); break;   // rotary tables [T, hd/2]
+        case 15: src = M->sinv; n = s.T * (s.hd / 2); break;
         default: return fail(MLB_E_INVALID_ARG, "unknown stage %d", stage);
     }
     *count = (size_t)n;

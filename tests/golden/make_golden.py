@@ -2,8 +2,8 @@
 
 Every value here comes from the CPU oracle (oracle/), run on the seeded inputs
 of bitwise_reproducible_fp32_amd.inputs; nothing is taken from the HIP path.
-Usage: python tests/golden/make_golden.py c0 c2 c3 c4 [--threads N]
-(c4, one full step of the 162M decoder, takes about three hours on 8 threads.)
+Usage: python tests/golden/make_golden.py c0 c2 c3 c4 tables [--threads N]
+(c4, two full steps of the 162M decoder, takes about three hours per step on 8 threads.)
 """
 from __future__ import annotations
 
@@ -22,6 +22,7 @@ import oracle  # noqa: E402
 from bitwise_reproducible_fp32_amd import inputs as I  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+TABLE_SEED = 20241
 
 
 def hx(x) -> str:
@@ -82,9 +83,32 @@ def main():
             cfg = I.make_config("c3")
             _, recs = run("c3", cfg, 3, log=print)
             out = dict(config="c3", cfg=cfg, init_seed=I.INIT_SEED, steps=recs)
+        elif name == "tables":
+            # Digests of the bytes that come from the host's binary64 libm (the
+            # rotary tables and the profile's seeded step-0 parameters) and of
+            # the seeded input parameters, per config: a host whose libm or
+            # numpy rounds one value differently fails against these loudly.
+            out = dict(config="tables", seed=TABLE_SEED, steps=[])
+            for c in ("c0", "c3", "c4"):
+                cfg = I.make_config(c)
+                cs, sn = oracle.rope_table(cfg["seq_len"], cfg["head_dim"], cfg["rope_theta"])
+                out[c] = dict(rope_cos=sha(cs), rope_sin=sha(sn),
+                              seeded_params=sha(oracle.seed_params(cfg, TABLE_SEED)),
+                              init_params=sha(I.init_params(cfg)))
+                print(c, out[c], flush=True)
         elif name == "c4":
+            # Steps 1 and 2 of the 162M decoder; the record is rewritten after
+            # each step so that step 1 is kept if step 2 is cut short.
             cfg = I.make_config("c4")
-            _, recs = run("c4", cfg, 1, log=lambda t: print(t, flush=True), log_micro=True)
+            model, recs = None, []
+            for s in (1, 2):
+                model, rec = run("c4", cfg, 1, model=model, start=s,
+                                 log=lambda t: print(t, flush=True), log_micro=True)
+                recs += rec
+                part = dict(config="c4", cfg=cfg, init_seed=I.INIT_SEED, steps=recs,
+                            oracle_threads=a.threads)
+                with open(os.path.join(HERE, "c4.json"), "w") as f:
+                    json.dump(part, f, indent=1)
             out = dict(config="c4", cfg=cfg, init_seed=I.INIT_SEED, steps=recs)
         else:
             raise SystemExit(f"unknown config {name}")
