@@ -66,7 +66,10 @@ typedef enum mlb_which { MLB_PARAMS = 0, MLB_GRAD = 1, MLB_ADAM_M = 2, MLB_ADAM_
 int64_t mlb_param_count(const mlb_config* cfg);
 
 /* Device bytes the arena must hold for cfg (params, gradient accumulator,
- * both moments, stored activations and scratch of one micro-batch). */
+ * both moments, stored activations and scratch of one micro-batch of
+ * batch x seq_len tokens; the model card's "Training" table runs 4 x 2,048).
+ * MLB_E_INVALID_ARG for an invalid config, MLB_E_UNSUPPORTED for a shape the
+ * kernels are not built for. Touches no device. */
 mlb_status mlb_workspace_bytes(const mlb_config* cfg, size_t* bytes);
 
 /* Creates a model on the current HIP device. init_params_host: host float32
@@ -85,11 +88,15 @@ mlb_status mlb_workspace_bytes(const mlb_config* cfg, size_t* bytes);
 mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init_params_host, void* dev_arena,
                     size_t arena_bytes, void* hip_stream, mlb_model** out);
 
-/* Forward pass and loss of one micro-batch: d_inputs and d_targets are device
- * int32 arrays of batch*seq_len ids (row-major [batch, seq_len]), read before
- * the call returns. Writes the shard loss (mean over the micro-batch) to
- * *out_loss_host and keeps the activations for mlb_backward. Synchronises the
- * stream. An id outside [0, vocab) gives MLB_E_BAD_TOKEN and no usable forward. */
+/* Forward pass and loss of one micro-batch (model card, "Training" table: the
+ * loss is the mean cross-entropy over the 4 x 2,048 tokens of a shard; the
+ * mojolearn project page counts cross-entropy in the verified chain):
+ * d_inputs and d_targets are device int32 arrays of batch*seq_len ids
+ * (row-major [batch, seq_len]; targets are the next ids), read before the call
+ * returns. Writes the shard loss to *out_loss_host and keeps the activations
+ * for mlb_backward. Synchronises the stream. An id outside [0, vocab) gives
+ * MLB_E_BAD_TOKEN (kernels read no table row for it) and no usable forward;
+ * the state is unchanged. */
 mlb_status mlb_forward_loss(mlb_model* m, const int32_t* d_inputs, const int32_t* d_targets, float* out_loss_host);
 
 /* Inference forward of one batch of [batch, seq_len] device int32 ids (model
@@ -110,26 +117,45 @@ mlb_status mlb_infer(mlb_model* m, const int32_t* d_inputs, const int32_t* d_tar
 mlb_status mlb_greedy_next(mlb_model* m, const int32_t* d_inputs, int position, int32_t* next_host);
 
 /* Backward of the last forward; folds its gradient g into the accumulator,
- * G = G + g (call order = micro-batch order). MLB_E_STATE without a forward. */
+ * G = G + g (call order = micro-batch order). The model card's "Training"
+ * table sums the 64 shard gradients of a step in a fixed order; this call is
+ * one term of that sum, and the order of calls is the order of the sum.
+ * MLB_E_STATE without a successful forward since the last backward (a second
+ * backward of one forward adds nothing and is refused). */
 mlb_status mlb_backward(mlb_model* m);
 
-/* One AdamW step with learning rate lr on the accumulated G, then G = +0.
- * MLB_E_STATE when no backward ran since the last step. */
+/* One AdamW step with learning rate lr on the accumulated G, then G = +0
+ * (model card, "Training" table: AdamW with beta (0.9, 0.95), eps 1e-8,
+ * weight decay 0.1; the learning rate of each step comes from the caller,
+ * who follows the table's warmup and cosine schedule). Step t = previous + 1;
+ * the bias corrections are RN(1 - beta^t) from a binary64 product. MLB_E_STATE
+ * when no backward ran since the last step; the state is then unchanged. */
 mlb_status mlb_adamw_step(mlb_model* m, float lr);
 
-/* Exact state bytes (MLBC v1): 256-byte header (magic "MLBCKPT1", format,
- * profile, config, step, parameter count, SHA-256 of params, m, v and of the
- * header itself) followed by params, m and v as little-endian float32. The
- * bytes are a pure function of the state. host_buf NULL: *len = size only.
- * MLB_E_STATE while gradients are pending; MLB_E_IO if cap is too small. */
+/* Exact state bytes (MLBC v1; model card, "Using the model": a checkpoint
+ * that a trainer is restored from and whose load verifies every array digest):
+ * 256-byte header (magic "MLBCKPT1", format, profile, config, step, parameter
+ * count, SHA-256 of params, m, v and of the header itself) followed by params,
+ * m and v as little-endian float32. The bytes are a pure function of the
+ * state. host_buf NULL: *len = size only. MLB_E_STATE while gradients are
+ * pending (between a backward and its AdamW step); MLB_E_IO if cap is too
+ * small (*len still receives the size). The caller owns host_buf. */
 mlb_status mlb_save(const mlb_model* m, void* host_buf, size_t cap, size_t* len);
 
-/* Restores params, moments and step from mlb_save bytes. Verifies magic,
- * format and profile (MLB_E_PROFILE_MISMATCH), config (MLB_E_CONFIG_MISMATCH),
- * size and every digest (MLB_E_CORRUPT) before touching the state. */
+/* Restores params, moments and step from mlb_save bytes (model card, "Using
+ * the model": restore from checkpoint bytes, verifying every array digest).
+ * Verifies magic, format and profile (MLB_E_PROFILE_MISMATCH), the header
+ * digest, padding, size and every array digest (MLB_E_CORRUPT) and the config
+ * (MLB_E_CONFIG_MISMATCH) before touching the state; a refused load leaves
+ * the state as it was. A successful load clears G and any pending forward.
+ * Synchronises the stream; host_buf is only read. */
 mlb_status mlb_load(mlb_model* m, const void* host_buf, size_t len);
 
-/* Copies a state array (mlb_param_count floats) to host memory. */
+/* Copies a state array (mlb_param_count floats, canonical order) to host
+ * memory, for the bit-for-bit comparisons the mojolearn PyPI page ("What
+ * bitwise identity means") makes the test of the identity claim.
+ * MLB_E_IO if bytes is smaller than the array; MLB_E_INVALID_ARG for an
+ * unknown array. Synchronises the stream. */
 mlb_status mlb_read(const mlb_model* m, mlb_which which, void* host_dst, size_t bytes);
 
 /* The parameters as a safetensors file image, for running the weights in
@@ -148,7 +174,9 @@ mlb_status mlb_safetensors(const mlb_config* cfg, const float* params_host, void
 /* Copies an activation of the last forward to host memory (stage ids: 0 layer
  * input, 1 attention-norm output, 2 its 1/rms, 3 q|k|v after rotation, 4 P,
  * 5 attention output, 6 mid-layer residual, 7 MLP-norm output, 8 its 1/rms,
- * 9 g|u, 10 SwiGLU output, 11 final hidden, 12 d-logits, 13 per-row losses).
+ * 9 g|u, 10 SwiGLU output, 11 final hidden, 12 d-logits, 13 per-row losses;
+ * 14 and 15 the rotary cos and sin tables [seq_len, head_dim/2] the model
+ * uploaded at mlb_init, available before any forward).
  * Layouts are row-major; P is dense [batch*heads, T, T] with +0 above the
  * diagonal; d-logits are [tokens, vocab]. *count receives the element count;
  * host_dst may be NULL to query it. */
