@@ -420,7 +420,10 @@ void k_gemm(KArgs a0, KArgs a1) {
     // operation, so the bits do not depend on the path.
     auto store_pair = [&](const v16f& v0, const v16f& v1, int64_t bi, bool valid) {
         const int mode = a.split ? 0 : emode;
-        if (!valid && mode == 1) return;   // no term in this chunk: unchanged
+        // a per-chunk launch leaves rows without a term in its chunk alone (the
+        // rule skips empty chunks); a whole contraction with no term is +0,
+        // so accumulate mode still stores C + (+0)
+        if (!valid && mode == 1 && a.chunk >= 0) return;
         const int64_t gj0 = j0 + j0l, gj1 = j0 + j1l;
         float* out = a.split ? a.part + gy * a.M * a.N : C;
         const int64_t ld = a.split ? a.N : a.ldc;

@@ -180,6 +180,26 @@ def test_causal_ranges(mlb, krange, T, hd):
         assert_bits(f"krange {krange} simple {simple} split {split}", host(C).reshape(T, hd), want)
 
 
+@pytest.mark.parametrize("a_kc", [False, True])
+def test_accumulate_rows_without_terms(mlb, a_kc):
+    """k >= i with more rows than K: rows i >= K have an empty contraction
+    (+0), and accumulate mode gives C + (+0) there, which turns -0 into +0, on
+    every launch form."""
+    rng = np.random.default_rng(31)
+    M, K, N = 300, 100, 40
+    A = make(rng, (M, K) if a_kc else (K, M))
+    B = make(rng, (K, N))
+    C0 = make(rng, (M, N))
+    C0[rng.random((M, N)) < 0.3] = -0.0
+    lda = K if a_kc else M
+    want = orc_contract(A, B, M, N, K, lda, a_kc, N, False, krange=2, mode=1, C0=C0)
+    assert np.any(np.signbit(C0[K:]) & (C0[K:] == 0)) and not np.any(np.signbit(want[K:]) & (want[K:] == 0))
+    for simple, split in ((0, -1), (0, 0), (0, 1), (1, -1)):
+        C = dev(C0.ravel())
+        mlb.gemm(dev(A), dev(B), C, M, N, K, lda, a_kc, N, False, N, krange=2, mode=1, simple=simple, split=split)
+        assert_bits(f"a_kc {a_kc} simple {simple} split {split}", host(C).reshape(M, N), want)
+
+
 def test_outmask_scores(mlb):
     rng = np.random.default_rng(9)
     T, hd = 300, 64
