@@ -79,35 +79,62 @@ def measured_traffic(kernel: str, cfg_name: str) -> float | None:
     return None
 
 
-def cpu_baseline(cfg_name: str, init: np.ndarray, seconds_hint: float) -> dict:
-    """The oracle as it stands, on a bounded sample of the workload: one
-    forward+backward of a 2 x seq_len micro-batch of the same model (half the
-    workload's micro-batch, same window length), with OpenMP across independent
-    outputs on this host's cores. The rate is scaled to tokens/s of the
-    benchmark workload by FLOPs per token."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_sample_rate(cfg: dict, cfg_name: str, batch: int, seq_len: int, init: np.ndarray,
+                       threads: int) -> dict:
+    """One forward+backward of the oracle on a batch x seq_len micro-batch of
+    the workload's model (same parameters), timed; the rate is scaled to
+    tokens/s of the workload by FLOPs per token."""
     import oracle
     from bitwise_reproducible_fp32_amd import inputs as I
-    cfg = I.make_config(cfg_name)
-    T = cfg["seq_len"]
-    Bs = min(2, cfg["batch"])
-    scfg = dict(cfg, batch=Bs, seq_len=T)
-    cores = min(16, len(os.sched_getaffinity(0)))
-    oracle.set_threads(cores)
+    scfg = dict(cfg, batch=batch, seq_len=seq_len)
+    oracle.set_threads(threads)
     m = oracle.Model(scfg, init)
     if cfg_name == "c0":
-        x, y = I.c0_batch(0, Bs, T)
+        x, y = I.c0_batch(0, batch, seq_len)
     else:
         x, y = I.zipf_batch(scfg, 0)
     t0 = time.perf_counter()
     m.forward(x, y)
     m.backward()
     dt = time.perf_counter() - t0
-    sample_flops = flops_per_token(scfg) * Bs * T
-    rate = sample_flops / dt
-    return {"value": rate / flops_per_token(cfg), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"oracle forward+backward of one {Bs}x{T}-token micro-batch of the {cfg_name} model "
-                      f"({dt:.1f} s, {rate / 1e9:.1f} GFLOP/s), scaled by FLOPs per token of the workload",
-            "gflops": rate / 1e9, "seconds": dt}
+    rate = flops_per_token(scfg) * batch * seq_len / dt
+    return {"tokens_per_s": rate / flops_per_token(cfg), "gflops": rate / 1e9, "seconds": dt,
+            "threads": threads, "sample": f"{batch}x{seq_len} tokens"}
+
+
+def cpu_baseline(cfg_name: str, init: np.ndarray) -> dict:
+    """The oracle as it stands, on bounded samples of the workload, on this
+    host's cores: all of the threads the process may use (OpenMP across
+    independent outputs; the OMP_NUM_THREADS share when it is set, else the
+    affinity mask), and one thread (the reference semantics). The all-thread
+    rate is the reported value."""
+    from bitwise_reproducible_fp32_amd import inputs as I
+    cfg = I.make_config(cfg_name)
+    T = cfg["seq_len"]
+    affinity = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or affinity
+    many = oracle_sample_rate(cfg, cfg_name, min(2, cfg["batch"]), T, init, threads)
+    one = oracle_sample_rate(cfg, cfg_name, 1, min(T, 128), init, 1)
+    return {"value": round(many["tokens_per_s"], 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle forward+backward of one {many['sample']} micro-batch of the {cfg_name} model on "
+                      f"{threads} threads ({many['seconds']:.1f} s, {many['gflops']:.1f} GFLOP/s), scaled to the "
+                      f"workload by FLOPs per token",
+            "cpu_model": cpu_model(), "affinity_cpus": affinity,
+            "one_thread": {"value": round(one["tokens_per_s"], 2), "unit": "tokens/s",
+                           "gflops": round(one["gflops"], 2), "seconds": round(one["seconds"], 1),
+                           "sample": f"oracle forward+backward of one {one['sample']} micro-batch on 1 thread"},
+            "gflops": round(many["gflops"], 1), "seconds": round(many["seconds"], 1)}
 
 
 def contraction_kernels(stats: list[dict]) -> dict[str, dict]:
@@ -301,7 +328,7 @@ def main() -> int:
     }
     if not a.no_cpu_baseline:
         try:
-            out["cpu_baseline"] = cpu_baseline(a.config, init, 20.0)
+            out["cpu_baseline"] = cpu_baseline(a.config, init)
         except Exception as e:  # the baseline is reported, never required
             out["cpu_baseline"] = {"error": str(e)}
     print(json.dumps(out), flush=True)
