@@ -89,6 +89,7 @@ _SIGS = {
     "mlb_prim_swiglu_bwd": (i32, [vp, vp, i64, i64, vp, vp]),
     "mlb_prim_cross_entropy": (i32, [vp, vp, i64, i64, vp, vp, vp, vp]),
     "mlb_prim_embed_scatter": (i32, [vp, vp, i64, i64, i64, vp, vp, sz, vp]),
+    "mlb_prim_embed_scatter_noalloc": (i32, [vp, vp, i64, i64, i64, vp, vp]),
     "mlb_prim_adamw": (i32, [vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i64, vp]),
     "mlb_prim_unary": (i32, [vp, vp, i64, i32, vp]),
     "mlb_diag_mfma": (i32, [i32, vp, vp, vp, vp, i64, vp]),

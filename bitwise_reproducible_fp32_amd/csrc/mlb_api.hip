@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <utility>
@@ -1566,6 +1567,42 @@ mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N
     const int r = mlb::embed_scatter(ids, dh, N, d, V, dE, dE, 0, static_cast<uint64_t*>(ws),
                                      static_cast<hipStream_t>(stream));
     return r == 0 ? MLB_OK : fail(MLB_E_INVALID_ARG, "embed_scatter (%d)", r);
+}
+
+// Allocation-free scatter: the sort keys live in a file-scope device array
+// (one copy per GPU, held until the process ends). Host code must not pass the
+// array's name to a kernel (on the host it is only a stand-in symbol): its
+// device address is looked up once per device with hipGetSymbolAddress and
+// that address is what the kernels receive.
+constexpr int64_t SCATTER_SCRATCH_KEYS = MAX_TOKENS;   // 64 KiB of sort keys
+static __device__ __align__(256) uint64_t scratch[SCATTER_SCRATCH_KEYS];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::once_flag g_scratch_once[MAX_DEVICES];
+uint64_t* g_scratch_ptr[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+}  // namespace
+
+mlb_status mlb_prim_embed_scatter_noalloc(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V,
+                                          float* dE, void* stream) {
+    if (!ids || !dh || !dE) return fail(MLB_E_INVALID_ARG, "null argument");
+    if (N < 0 || d <= 0 || V <= 0) return fail(MLB_E_INVALID_ARG, "sizes N %ld, d %ld, V %ld", (long)N, (long)d, (long)V);
+    if (N > SCATTER_SCRATCH_KEYS)
+        return fail(MLB_E_UNSUPPORTED, "%ld positions: the static scratch holds the keys of at most %ld", (long)N,
+                    (long)SCATTER_SCRATCH_KEYS);
+    int dev = 0;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(MLB_E_DEVICE, "device %d beyond the scratch table", dev);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = static_cast<uint64_t*>(ptr);
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+        return fail(MLB_E_DEVICE, "scratch address on device %d: %s", dev, hipGetErrorString(g_scratch_err[dev]));
+    const int r = mlb::embed_scatter(ids, dh, N, d, V, dE, dE, 0, g_scratch_ptr[dev], static_cast<hipStream_t>(stream));
+    return r == 0 ? MLB_OK : fail(MLB_E_DEVICE, "embed_scatter (%d)", r);
 }
 
 mlb_status mlb_prim_adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float beta1, float beta2,

@@ -107,6 +107,17 @@ mlb_status mlb_prim_cross_entropy(const float* logits, const int32_t* targets, i
 mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, float* dE,
                                   void* ws, size_t ws_bytes, void* hip_stream);
 
+/* The embedding-gradient scatter above without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the sort keys live in
+ * a static device array of the library (64 KiB per GPU, held until the process
+ * ends), so the call allocates nothing. Same arguments, rule and bits as
+ * mlb_prim_embed_scatter. N above 8,192 gives MLB_E_UNSUPPORTED. Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (several
+ * streams or threads at once) race and must not be made. */
+mlb_status mlb_prim_embed_scatter_noalloc(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V,
+                                          float* dE, void* hip_stream);
+
 /* AdamW (model card "Training" table: beta (0.9, 0.95), eps 1e-8, wd 0.1),
  * coupled form, step t >= 1: bias corrections RN(1 - beta^t) from a binary64
  * product. Updates p, m, v in place and sets g to +0. */
