@@ -783,6 +783,7 @@ void orc_fma_array(const float* a, const float* b, const float* c, float* y, int
     for (int64_t i = 0; i < n; ++i) y[i] = std::fma(a[i], b[i], c[i]);
 }
 void orc_sigmoid_array(const float* x, float* y, int64_t n) {
+#pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int64_t i = 0; i < n; ++i) y[i] = sigmoid_p(x[i]);
 }
 

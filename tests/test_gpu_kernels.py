@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_bits, dev, empty, host
+from gpu_util import assert_bits, bits_equal, dev, diff_report, empty, host
 
 pytestmark = pytest.mark.gpu
 
@@ -78,12 +78,40 @@ SPECIAL = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 
                     0x3F800000, 0xBF800000, 0x3F317218, 0xBF317218], dtype=np.uint32)
 
 
+def test_elementary_spellings_match_oracle_on_every_input(mlb):
+    """exp, log, the branch-free exp the cross-entropy uses and the sigmoid on
+    all 2^32 binary32 inputs, in chunks of 2^28, against the oracle bit for
+    bit (NaN payloads canonicalised)."""
+    import os
+    import torch
+    oracle.set_threads(min(16, len(os.sched_getaffinity(0))))
+    chunk = 1 << 28
+    y = empty(chunk)
+    names = ["exp", "log", "sigmoid", "exp (branch-free)"]
+    try:
+        for c in range(1 << 32 >> 28):
+            x = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64).astype(np.uint32).view(np.float32)
+            xd = dev(x)
+            want_exp = oracle.exp(x)
+            want = {0: want_exp, 3: want_exp, 1: oracle.log(x)}
+            want[2] = np.empty_like(x)
+            oracle.lib().orc_sigmoid_array(x, want[2], x.size)
+            for which in (0, 3, 1, 2):
+                mlb.unary(xd, y, chunk, which)
+                got = host(y)
+                if not bits_equal(got, want[which]):
+                    raise AssertionError(f"chunk {c}: " + diff_report(names[which], got, want[which]))
+            del xd
+            torch.cuda.synchronize()
+    finally:
+        oracle.set_threads(1)
+
+
 @pytest.mark.parametrize("which", [0, 1, 2, 3])
-def test_elementary_spellings_match_oracle(mlb, which):
-    """Every 257th bit pattern and the special inputs; spelling 3 is exp in
-    its branch-free form and must give exp's bits."""
-    u = np.concatenate([np.arange(0, 1 << 32, 257, dtype=np.uint64).astype(np.uint32), SPECIAL])
-    x = u.view(np.float32)
+def test_elementary_spellings_special_inputs(mlb, which):
+    """The special inputs on their own: signed zeros, infinities, NaNs, the
+    range ends of exp and their neighbours, subnormals."""
+    x = SPECIAL.view(np.float32)
     y = empty(x.size)
     mlb.unary(dev(x), y, x.size, which)
     if which == 2:
