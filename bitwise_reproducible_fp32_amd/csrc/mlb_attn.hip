@@ -291,6 +291,9 @@ void k_attn_av(AvArgs a) {
         store_lds();
         __syncthreads();
         if (st + 1 < nsteps) load(st + 1);
+        // higher issue priority while this wave has matrix work (the waves of
+        // the other workgroups on the SIMD are then staging or waiting)
+        __builtin_amdgcn_s_setprio(1);
         if (sl > 0 && k0 % 1024 == 0 && dirty) {   // a new chunk: fold the finished one
 #pragma unroll
             for (int e = 0; e < 16; ++e) { tot[e] = have ? tot[e] + acc[e] : acc[e]; acc[e] = 0.0f; }
@@ -332,6 +335,7 @@ void k_attn_av(AvArgs a) {
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         const bool last = (st + 1 == nsteps) || (st + 1 == na);
         if (last) {   // the tile's outputs: fold the last chunk, (rotate,) store, reset
             float v[16];

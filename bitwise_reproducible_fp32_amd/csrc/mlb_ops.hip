@@ -165,52 +165,54 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx_reg(const float* __restr
 // Per-chunk column partials of the gain gradient: for column c and chunk ch
 // (rows [1024 ch, 1024 ch + 1024)), part[ch][c] is an fma chain from +0 over
 // the chunk's rows in ascending order of dy[n][c] * (x[n][c] * r[n]). There
-// are only d * chunks serial chains, so a workgroup owns DW_CW columns of one
-// chunk: all four waves stage 128-row blocks of dy and x * r in LDS (two
-// buffers, the next block loading while the current one is used) and the
-// first DW_CW lanes run the column chains through them. 32 columns per
-// workgroup put twice as many workgroups (and loads) in flight as 64 (8,192 x
-// 768: 41 instead of 49 us for the whole RMSNorm backward; 16 is no faster).
-constexpr int DW_RB = 128;
-constexpr int DW_CW = 32;   // columns (chains) per workgroup
+// are only d * chunks serial chains, so the loads, not the chains, set the
+// time: a workgroup owns DW_CW columns of one chunk, and its sixteen waves
+// stage DW_RB-row blocks of dy and x * r in LDS (two buffers) with the loads
+// of the block after next already in flight (two register sets), while the
+// first DW_CW lanes run the column chains through the staged block.
+constexpr int DW_RB = 256;
+constexpr int DW_CW = 32;      // columns (chains) per workgroup
+constexpr int DW_THREADS = 1024;
 template <int CW>
-__global__ __launch_bounds__(256) void k_rmsnorm_dw_part(const float* __restrict__ dy, const float* __restrict__ x,
-                                                        const float* __restrict__ r, int64_t rows, int64_t d,
-                                                        float* __restrict__ part) {
-    constexpr int RS = 256 / CW;   // row groups of the staging loads
+__global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __restrict__ dy,
+                                                               const float* __restrict__ x,
+                                                               const float* __restrict__ r, int64_t rows, int64_t d,
+                                                               float* __restrict__ part) {
+    constexpr int RS = DW_THREADS / CW;   // rows covered by one pass of the threads
+    constexpr int PER = DW_RB / RS;       // values of each array per thread per block
     __shared__ float sy[2][DW_RB][CW + 1], sx[2][DW_RB][CW + 1];
     const int tid = threadIdx.x, col = tid % CW, rsub = tid / CW;
     const int64_t c = (int64_t)blockIdx.x * CW + col;
     const bool live = c < d;
     const int64_t n0 = (int64_t)blockIdx.y * KC, n1 = (n0 + KC < rows) ? n0 + KC : rows;
     const int64_t nb = (n1 - n0 + DW_RB - 1) / DW_RB;
-    float vy[DW_RB / RS], vx[DW_RB / RS];
+    // raw loads (x * r is formed at the LDS store, so that nothing waits for
+    // a load before the block after next is issued)
+    float ya[PER], xa[PER], ra[PER], yb[PER], xb[PER], rb[PER];
     // Unconditional loads from clamped positions (a guarded load became a
     // branch with a wait per row): rows past the chunk are never taken by
     // the chain and columns past d are never stored.
     const int64_t cc = live ? c : d - 1;
-    auto load = [&](int64_t b) __attribute__((always_inline)) {
+    auto load = [&](int64_t b, float (&vy)[PER], float (&vx)[PER], float (&vr)[PER]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < DW_RB / RS; ++q) {
+        for (int q = 0; q < PER; ++q) {
             int64_t n = n0 + b * DW_RB + rsub + RS * q;
             n = n < n1 ? n : n1 - 1;
             vy[q] = dy[n * d + cc];
-            vx[q] = x[n * d + cc] * r[n];
+            vx[q] = x[n * d + cc];
+            vr[q] = r[n];
         }
     };
-    auto store = [&](int buf) __attribute__((always_inline)) {
+    auto store = [&](int buf, const float (&vy)[PER], const float (&vx)[PER], const float (&vr)[PER])
+        __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < DW_RB / RS; ++q) {
+        for (int q = 0; q < PER; ++q) {
             sy[buf][rsub + RS * q][col] = vy[q];
-            sx[buf][rsub + RS * q][col] = vx[q];
+            sx[buf][rsub + RS * q][col] = vx[q] * vr[q];
         }
     };
     float acc = 0.0f;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int64_t b = 0; b < nb; ++b) {
-        if (b + 1 < nb) load(b + 1);
+    auto chain = [&](int64_t b) __attribute__((always_inline)) {
         if (tid < CW) {
             const int64_t len = (n1 - n0 - b * DW_RB) < DW_RB ? (n1 - n0 - b * DW_RB) : DW_RB;
             const int buf = (int)(b & 1);
@@ -221,7 +223,28 @@ __global__ __launch_bounds__(256) void k_rmsnorm_dw_part(const float* __restrict
                 for (int k = 0; k < len; ++k) acc = __builtin_fmaf(sy[buf][k][col], sx[buf][k][col], acc);
             }
         }
-        if (b + 1 < nb) store((int)((b + 1) & 1));
+    };
+    // block b is staged in buffer b & 1; the registers alternate between
+    // block b + 1 (set a for even b) and block b + 2 (the other set)
+    // Loads past the last block re-read the last block (in bounds, never
+    // chained): every iteration issues the same loads, so the hardware's
+    // in-order load counter lets each store wait for its own set only.
+    auto blk = [&](int64_t b) -> int64_t { return b < nb ? b : nb - 1; };
+    load(0, ya, xa, ra);
+    load(blk(1), yb, xb, rb);
+    store(0, ya, xa, ra);
+    __syncthreads();
+    for (int64_t b = 0; b < nb; b += 2) {
+        // even b: set a is free, set b holds block b + 1
+        load(blk(b + 2), ya, xa, ra);
+        chain(b);
+        store(1, yb, xb, rb);
+        __syncthreads();
+        if (b + 1 >= nb) break;
+        // odd b + 1: set b is free, set a holds block b + 2
+        load(blk(b + 3), yb, xb, rb);
+        chain(b + 1);
+        store(0, ya, xa, ra);
         __syncthreads();
     }
     if (tid < CW && live) part[blockIdx.y * d + c] = acc;
@@ -892,7 +915,7 @@ int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows
         return ok();
     }
     const int64_t nch = (rows + KC - 1) / KC;
-    k_rmsnorm_dw_part<DW_CW><<<dim3(blocks(d, DW_CW), (unsigned)nch), 256, 0, s>>>(dy, x, r, rows, d, part);
+    k_rmsnorm_dw_part<DW_CW><<<dim3(blocks(d, DW_CW), (unsigned)nch), DW_THREADS, 0, s>>>(dy, x, r, rows, d, part);
     k_fold_cols<<<blocks(d, 256), 256, 0, s>>>(part, nch, d, dw, mode);
     return ok();
 }
