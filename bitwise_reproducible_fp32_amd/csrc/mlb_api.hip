@@ -235,6 +235,7 @@ struct mlb_model {
     hipStream_t stream;        // the caller's stream: every call is ordered on it
     hipStream_t side = nullptr;
     hipStream_t cur = nullptr; // the stream the op being enqueued runs on
+    hipEvent_t sorted = nullptr;   // the embedding keys of the last training forward are sorted (side stream)
     bool overlap = false;      // backward weight-gradient work on the side stream (off: one stream is faster)
     std::vector<hipEvent_t> sync_pool;
     size_t sync_next = 0;
@@ -274,6 +275,7 @@ namespace {
 mlb_status make_streams(mlb_model* M) {
     if (hipStreamCreateWithFlags(&M->side, hipStreamNonBlocking) != hipSuccess)
         return fail(MLB_E_DEVICE, "side stream");
+    if (hipEventCreateWithFlags(&M->sorted, hipEventDisableTiming) != hipSuccess) return fail(MLB_E_DEVICE, "event");
     M->sync_pool.assign(64, nullptr);
     for (hipEvent_t& e : M->sync_pool)
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return fail(MLB_E_DEVICE, "event");
@@ -294,6 +296,8 @@ void release_streams(mlb_model* M) {
     for (Ring* r : {&M->dh, &M->dgu, &M->dxn, &M->dqkv})
         for (hipEvent_t e : r->ev)
             if (e) (void)hipEventDestroy(e);
+    if (M->sorted) (void)hipEventDestroy(M->sorted);
+    M->sorted = nullptr;
     if (M->side) (void)hipStreamDestroy(M->side);
     M->side = nullptr;
     M->sync_pool.clear();
@@ -584,6 +588,8 @@ mlb::GemmDesc head_gemm(const Sizes& s) {
 
 // mode 0: training (loss, d-logits in place of the logits); 1: inference with
 // loss (the logits are kept); 2: inference, logits only.
+mlb_status stream_wait(mlb_model* M, hipStream_t from, hipStream_t to);
+
 mlb_status forward(mlb_model* M, int mode = 0) {
     const Sizes& s = M->s;
     hipStream_t st = M->stream;
@@ -591,6 +597,16 @@ mlb_status forward(mlb_model* M, int mode = 0) {
     const int64_t N = s.N, d = s.d, F = s.F, T = s.T, H = s.H, hd = s.hd, BH = s.B * s.H;
     const double f4 = 4.0, tri = (double)BH * (double)T * (double)(T + 1) / 2.0;
     OP("embed_gather", f4 * 2 * N * d, mlb::gather_rows(M->ids, M->p + M->offE, s.V, d, N, M->h[0], M->err, st));
+    if (mode == 0) {
+        // the embedding gradient's key sort needs the ids only: it runs on the
+        // side stream beside the forward and is joined by the backward's scatter
+        const mlb_status ws = stream_wait(M, st, M->side);
+        if (ws != MLB_OK) return ws;
+        M->cur = M->side;
+        OP("embed_sort", f4 * N, mlb::embed_sort(M->ids, N, s.V, M->keys, M->side));
+        if (hipEventRecord(M->sorted, M->side) != hipSuccess) return fail(MLB_E_DEVICE, "sort event");
+        M->cur = st;
+    }
     for (int64_t l = 0; l < s.L; ++l) {
         OP("rmsnorm_fwd", f4 * (2 * N * d + N + d),
            mlb::rmsnorm_fwd(M->h[l], M->p + M->o_w1[l], N, d, M->cfg.rms_eps, M->xn1[l], M->r1[l], st));
@@ -795,13 +811,14 @@ mlb_status backward(mlb_model* M) {
     }
     // embedding rows in token order (tied: on top of the head gradient, then folded)
     CHK(to_side());
+    if (hipStreamWaitEvent(ss, M->sorted, 0) != hipSuccess) return fail(MLB_E_DEVICE, "sort wait");
     if (s.tied) {
         OP("embed_scatter", f4 * 3 * N * d,
-           mlb::embed_scatter(M->ids, DH.buf[kh], N, d, s.V, M->gE, M->gE, 0, M->keys, ss));
+           mlb::embed_scatter_sorted(M->keys, DH.buf[kh], N, d, s.V, M->gE, M->gE, 0, ss));
         OP("embed_fold", f4 * 3 * s.V * d, mlb::add_inplace(M->G + M->offE, M->gE, s.V * d, ss));
     } else {
         OP("embed_scatter", f4 * 3 * N * d,
-           mlb::embed_scatter(M->ids, DH.buf[kh], N, d, s.V, nullptr, M->G + M->offE, 1, M->keys, ss));
+           mlb::embed_scatter_sorted(M->keys, DH.buf[kh], N, d, s.V, nullptr, M->G + M->offE, 1, ss));
     }
     // join: the caller's stream continues after all side work
     on_main();

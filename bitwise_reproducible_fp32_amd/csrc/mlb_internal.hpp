@@ -167,6 +167,12 @@ int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s
 // src_init is null, else src_init[v]. keys must hold 2*N uint64 values.
 int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V,
                   const float* src_init, float* dst, int mode, uint64_t* keys, hipStream_t s);
+// The two halves of embed_scatter: the key sort (which depends on the ids
+// only, so it can run early, on another stream) and the segment walk over
+// keys that embed_sort wrote for the same ids, N and V.
+int embed_sort(const int32_t* ids, int64_t N, int64_t V, uint64_t* keys, hipStream_t s);
+int embed_scatter_sorted(const uint64_t* keys, const float* dh, int64_t N, int64_t d, int64_t V,
+                         const float* src_init, float* dst, int mode, hipStream_t s);
 // out = out + x elementwise (n floats).
 int add_inplace(float* out, const float* x, int64_t n, hipStream_t s);
 int adamw(float* p, float* g, float* m, float* v, int64_t n, float lr, float b1, float b2, float eps,

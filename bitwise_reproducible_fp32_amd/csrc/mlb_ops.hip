@@ -6,6 +6,8 @@
 // All of these kernels are bound by HBM bandwidth, so they read each input
 // once or a few times with coalesced 64-lane accesses; none uses atomics on
 // floating-point data.
+#include <type_traits>
+
 #include "mlb_device.hpp"
 #include "mlb_internal.hpp"
 
@@ -794,6 +796,148 @@ __global__ __launch_bounds__(256) void k_scatter_segments(const uint64_t* __rest
     *o = mode ? *o + acc : acc;
 }
 
+// The same sort on 32-bit keys (id << 13 | n) when ids are below 2^19 - 1
+// and positions below 8,192; invalid ids become 0xFFFFFFFF (never a valid
+// key) and sort last. The keys are distinct, so the result is unique and
+// equal to the 64-bit sort's order. Each of 1,024 threads holds 8 consecutive
+// keys: compare-exchange stages with stride below 8 run in registers, strides
+// 8 to 256 (partners in the same wavefront) through lane shuffles, and only
+// strides of 512 and more go through LDS with barriers.
+constexpr int SORT32_THREADS = 1024, SORT32_PER = 8;   // 8,192 slots
+__global__ __launch_bounds__(SORT32_THREADS) void k_sort_keys32(const int32_t* __restrict__ ids, int64_t N, int64_t V,
+                                                               uint32_t* __restrict__ out) {
+    __shared__ uint32_t lds[SORT32_THREADS * SORT32_PER];
+    const int t = threadIdx.x;
+    uint32_t k[SORT32_PER];
+#pragma unroll
+    for (int r = 0; r < SORT32_PER; ++r) {
+        const int q = SORT32_PER * t + r;
+        uint32_t key = 0xFFFFFFFFu;
+        if (q < N) {
+            const int32_t id = ids[q];
+            if (id >= 0 && id < V) key = ((uint32_t)id << 13) | (uint32_t)q;
+        }
+        k[r] = key;
+    }
+    // one compare-exchange of element i (value a) with its partner's value b
+    auto keep = [](uint32_t a, uint32_t b, bool lower, bool up) -> uint32_t {
+        const uint32_t lo = a < b ? a : b, hi = a < b ? b : a;
+        return (lower == up) ? lo : hi;
+    };
+    // stages whose partner sits in this thread's registers: compile-time
+    // strides, so the key array stays in registers
+    auto reg_stage = [&](auto stride_c, int size) __attribute__((always_inline)) {
+        constexpr int stride = decltype(stride_c)::value;
+#pragma unroll
+        for (int r = 0; r < SORT32_PER; ++r) {
+            if ((r & stride) != 0) continue;
+            const int i = SORT32_PER * t + r;
+            const uint32_t a = k[r], b = k[r + stride];
+            const bool up = (i & size) == 0;
+            k[r] = keep(a, b, true, up);
+            k[r + stride] = keep(b, a, false, up);
+        }
+    };
+    for (int size = 2; size <= SORT32_THREADS * SORT32_PER; size <<= 1) {
+        for (int stride = size >> 1; stride >= SORT32_PER; stride >>= 1) {
+            if (stride >= 64 * SORT32_PER) {
+                // partner in another wavefront: exchange through LDS
+#pragma unroll
+                for (int r = 0; r < SORT32_PER; ++r) lds[SORT32_PER * t + r] = k[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < SORT32_PER; ++r) {
+                    const int i = SORT32_PER * t + r;
+                    k[r] = keep(k[r], lds[i ^ stride], (i & stride) == 0, (i & size) == 0);
+                }
+                __syncthreads();
+            } else if (stride >= SORT32_PER) {
+                // partner in another lane of this wavefront
+                const int lx = stride / SORT32_PER;
+#pragma unroll
+                for (int r = 0; r < SORT32_PER; ++r) {
+                    const int i = SORT32_PER * t + r;
+                    const uint32_t b = (uint32_t)__shfl_xor((int)k[r], lx, 64);
+                    k[r] = keep(k[r], b, (i & stride) == 0, (i & size) == 0);
+                }
+            }
+        }
+        if (size > 4) reg_stage(std::integral_constant<int, 4>{}, size);
+        if (size > 2) reg_stage(std::integral_constant<int, 2>{}, size);
+        reg_stage(std::integral_constant<int, 1>{}, size);
+    }
+#pragma unroll
+    for (int r = 0; r < SORT32_PER; ++r) out[SORT32_PER * t + r] = k[r];
+}
+
+// For each segment head q of the 32-bit sorted keys (the first key of an id):
+// acc = init(v); for the segment's positions n in ascending order
+// acc = acc + dh[n][c]; then write. The segment's positions are staged in LDS
+// first; the rows of two batches of SEG_U terms are in flight while the
+// previous batch is added (loads past the segment repeat its last position
+// and are never added).
+constexpr int SEG_U = 32;
+__global__ __launch_bounds__(256) void k_scatter_segments32(const uint32_t* __restrict__ key, int64_t N,
+                                                            const float* __restrict__ dh, int64_t d,
+                                                            const float* src_init, float* dst, int mode) {
+    __shared__ uint32_t pos[SORT32_THREADS * SORT32_PER];
+    const int64_t q = blockIdx.x;
+    const uint32_t kq = key[q];
+    if (kq == 0xFFFFFFFFu) return;
+    const uint32_t v = kq >> 13;
+    if (q > 0 && (key[q - 1] >> 13) == v) return;    // not the head of its segment
+    const int tid = threadIdx.x, lane = tid & 63;
+    // segment length: 64 keys per step, the first key of another id ends it
+    int64_t len = 0;
+    for (int64_t e0 = q;; e0 += 64) {
+        const int64_t e = e0 + lane;
+        const bool same = e < N && key[e] != 0xFFFFFFFFu && (key[e] >> 13) == v;
+        const uint64_t m = __ballot(same);
+        if (~m != 0) { len = e0 - q + (int64_t)__builtin_ctzll(~m); break; }
+        if (e0 + 64 >= N) { len = N - q; break; }
+    }
+    for (int64_t e = tid; e < len; e += 256) pos[e] = key[q + e] & 0x1FFFu;
+    __syncthreads();
+    const int64_t c = (int64_t)blockIdx.y * 256 + tid;
+    if (c >= d) return;
+    float acc = src_init ? src_init[(int64_t)v * d + c] : 0.0f;
+    float ba[SEG_U], bb[SEG_U];
+    auto load = [&](int64_t e0, float (&b)[SEG_U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < SEG_U; ++u) {
+            const int64_t e = e0 + u < len ? e0 + u : len - 1;
+            b[u] = dh[(int64_t)pos[e] * d + c];
+        }
+    };
+    auto add = [&](int64_t e0, const float (&b)[SEG_U]) __attribute__((always_inline)) {
+        if (e0 + SEG_U <= len) {
+#pragma unroll
+            for (int u = 0; u < SEG_U; ++u) acc = acc + b[u];
+        } else {
+            for (int u = 0; u < SEG_U && e0 + u < len; ++u) acc = acc + b[u];
+        }
+    };
+    if (len <= SEG_U) {   // short segments (most of them): one batch, no padding loads
+#pragma unroll
+        for (int u = 0; u < SEG_U; ++u)
+            if (u < len) ba[u] = dh[(int64_t)pos[u] * d + c];
+        for (int u = 0; u < len; ++u) acc = acc + ba[u];
+        float* o = dst + (int64_t)v * d + c;
+        *o = mode ? *o + acc : acc;
+        return;
+    }
+    load(0, ba);
+    for (int64_t e0 = 0; e0 < len; e0 += 2 * SEG_U) {
+        load(e0 + SEG_U, bb);
+        add(e0, ba);
+        if (e0 + SEG_U >= len) break;
+        load(e0 + 2 * SEG_U, ba);
+        add(e0 + SEG_U, bb);
+    }
+    float* o = dst + (int64_t)v * d + c;
+    *o = mode ? *o + acc : acc;
+}
+
 __global__ __launch_bounds__(256) void k_add(float* out, const float* __restrict__ x, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = out[i] + x[i];
@@ -1008,15 +1152,38 @@ int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s
     return ok();
 }
 
-int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, const float* src_init,
-                  float* dst, int mode, uint64_t* keys, hipStream_t s) {
-    if (N < 0 || d <= 0 || V <= 0 || N > SORT_MAX) return -2;
+static bool keys32(int64_t N, int64_t V) { return V < (1 << 19) - 1 && N <= SORT32_THREADS * SORT32_PER; }
+
+int embed_sort(const int32_t* ids, int64_t N, int64_t V, uint64_t* keys, hipStream_t s) {
+    if (N < 0 || V <= 0 || N > SORT_MAX) return -2;
     if (N == 0) return 0;
+    if (keys32(N, V)) {
+        k_sort_keys32<<<1, SORT32_THREADS, 0, s>>>(ids, N, V, reinterpret_cast<uint32_t*>(keys));
+        return ok();
+    }
     int64_t P = 1;
     while (P < N) P <<= 1;
     k_sort_keys<<<1, 1024, 0, s>>>(ids, N, V, P, keys);
-    k_scatter_segments<<<dim3((unsigned)N, blocks(d, 256)), 256, 0, s>>>(keys, N, dh, d, src_init, dst, mode);
     return ok();
+}
+
+int embed_scatter_sorted(const uint64_t* keys, const float* dh, int64_t N, int64_t d, int64_t V,
+                         const float* src_init, float* dst, int mode, hipStream_t s) {
+    if (N < 0 || d <= 0 || V <= 0 || N > SORT_MAX) return -2;
+    if (N == 0) return 0;
+    if (keys32(N, V))
+        k_scatter_segments32<<<dim3((unsigned)N, blocks(d, 256)), 256, 0, s>>>(
+            reinterpret_cast<const uint32_t*>(keys), N, dh, d, src_init, dst, mode);
+    else
+        k_scatter_segments<<<dim3((unsigned)N, blocks(d, 256)), 256, 0, s>>>(keys, N, dh, d, src_init, dst, mode);
+    return ok();
+}
+
+int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, const float* src_init,
+                  float* dst, int mode, uint64_t* keys, hipStream_t s) {
+    if (N < 0 || d <= 0 || V <= 0 || N > SORT_MAX) return -2;
+    const int r = embed_sort(ids, N, V, keys, s);
+    return r ? r : embed_scatter_sorted(keys, dh, N, d, V, src_init, dst, mode, s);
 }
 
 int add_inplace(float* out, const float* x, int64_t n, hipStream_t s) {
