@@ -320,16 +320,19 @@ __global__ __launch_bounds__(256) void k_rope4(float* x, uint32_t npairs4, uint3
 
 // exp_p without branches, bit for bit the same function: the reduction and
 // polynomial run on 0 in place of a NaN or out-of-range input and the special
-// result is selected at the end; the scale 2^k is applied as (p * s1) * s2
-// with s2 = 1 in the normal range, where multiplying by 1 is exact. For code
-// that evaluates many exponentials per thread, where the branches of exp_p
-// would each hold an exec mask.
+// result is selected at the end. Two steps use single instructions that give
+// exactly the spelled values: the round-to-nearest-even of t (rndne; the
+// spelling's (t + 1.5 * 2^23) - 1.5 * 2^23 rounds |t| < 2^22 to the nearest
+// integer, ties to even, exactly) and the scaling p * 2^k (ldexp, one correct
+// rounding; the spelling multiplies by two powers of two of which only the
+// second can round). For code that evaluates many exponentials per thread,
+// where the branches of exp_p would each hold an exec mask; every binary32
+// input is checked against the oracle's exp.
 __device__ __forceinline__ float exp_p_select(float x) {
     const bool nan = x != x, hi = x >= u2f(0x42B17218u), lo = x <= u2f(0xC2CFF1B5u);
     const float xs = (nan || hi || lo) ? 0.0f : x;
-    const float shifter = 12582912.0f;
     const float t = xs * u2f(0x3FB8AA3Bu);
-    const float kf = (t + shifter) - shifter;
+    const float kf = __builtin_rintf(t);
     const int ki = (int)kf;
     float r = __builtin_fmaf(-kf, u2f(0x3F317200u), xs);
     r = __builtin_fmaf(-kf, u2f(0x35BFBE8Eu), r);
@@ -341,10 +344,7 @@ __device__ __forceinline__ float exp_p_select(float x) {
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    const bool big = ki > 127, small = ki < -126;
-    const float s1 = big ? u2f(0x7F000000u) : u2f((uint32_t)(small ? ki + 253 : ki + 127) << 23);
-    const float s2 = big ? 2.0f : (small ? u2f(0x00800000u) : 1.0f);
-    const float v = (p * s1) * s2;
+    const float v = __builtin_ldexpf(p, ki);
     return nan ? x : (hi ? __builtin_inff() : (lo ? 0.0f : v));
 }
 
