@@ -120,6 +120,24 @@ def test_c3_three_steps_bit_exact(overlap):
     compare(recs, gold["steps"])
 
 
+@pytest.mark.skipif(not os.path.exists(os.path.join(GOLD, "c4.json")), reason="no oracle record of the 162M steps")
+def test_c4_whole_steps_bit_exact():
+    """The 162M decoder's optimizer steps as the benchmark runs them (model
+    card, "Training" table: 64 shards of 4 x 2,048 tokens whose gradients are
+    summed in a fixed order, then AdamW at the schedule's learning rate): all
+    64 shard losses, the accumulated gradient, the parameters, both moments
+    and the checkpoint bytes of each recorded step equal the oracle's."""
+    gold = golden("c4")
+    cfg = I.make_config("c4")
+    import bitwise_reproducible_fp32_amd as mlb
+    m = mlb.Model(cfg, I.init_params(cfg))
+    for rec in gold["steps"]:
+        _, got = run_gpu("c4", cfg, 1, model=m, start=rec["step"], overlap=False)
+        print(f"c4 step {rec['step']}: loss0 {got[0]['losses'][0]}", flush=True)
+        compare(got, [rec])
+    m.close()
+
+
 @pytest.mark.parametrize("name", ["c0", "c3", "c4"])
 def test_seeded_init_matches_oracle(name):
     """With no step-0 parameters the library draws them from the seed; every
