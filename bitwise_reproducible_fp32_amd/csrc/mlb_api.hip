@@ -131,7 +131,7 @@ void sha256_bytes(const void* p, size_t n, uint8_t out[32]) {
 // ------------------------------------------------------------ layout
 constexpr size_t ALIGN = 256;
 constexpr int64_t KCH = 1024;
-constexpr int64_t MAX_TOKENS = 8192;
+constexpr int64_t MAX_TOKENS = mlb::EMBED_MAX_POSITIONS;   // 65,536 tokens per micro-batch
 
 struct Sizes {
     int64_t V, d, L, H, hd, F, B, T, N, P;
@@ -158,7 +158,7 @@ bool cfg_supported(const mlb_config* c, std::string* why) {
     if (c->d_model % 32 || c->ffn_hidden % 32) { *why = "d_model and ffn_hidden must be multiples of 32"; return false; }
     if (c->seq_len % 32) { *why = "seq_len must be a multiple of 32 (32x32 attention tiles)"; return false; }
     if ((uint64_t)c->batch * c->seq_len > (uint64_t)MAX_TOKENS) {
-        *why = "more than 8192 tokens per micro-batch";
+        *why = "more than 65,536 tokens per micro-batch";
         return false;
     }
     if (c->vocab > 0x7fffffffu) { *why = "vocab too large"; return false; }
@@ -351,7 +351,7 @@ size_t carve(mlb_model* M, char* base) {
     M->split = c.take<float>(M->split_n > 0 ? M->split_n : 1);
     M->split_side = c.take<float>(M->split_n > 0 ? M->split_n : 1);
     M->dwpart = c.take<float>(((s.N + KCH - 1) / KCH) * s.d);
-    M->keys = c.take<uint64_t>(2 * MAX_TOKENS);
+    M->keys = c.take<uint64_t>(mlb::embed_key_slots(s.N));
     return c.off + ALIGN;
 }
 
@@ -1579,8 +1579,9 @@ mlb_status mlb_prim_cross_entropy(const float* logits, const int32_t* targets, i
 mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, float* dE,
                                   void* ws, size_t ws_bytes, void* stream) {
     if (!ids || !dh || !dE) return fail(MLB_E_INVALID_ARG, "null argument");
-    if (N > MAX_TOKENS) return fail(MLB_E_UNSUPPORTED, "more than 8192 positions");
-    if (!ws || ws_bytes < (size_t)2 * MAX_TOKENS * 8) return fail(MLB_E_ARENA_TOO_SMALL, "scatter needs 131072 bytes");
+    if (N > MAX_TOKENS) return fail(MLB_E_UNSUPPORTED, "%ld positions: at most 65,536", (long)N);
+    const size_t need = 8 * (size_t)std::max<int64_t>(2 * 8192, mlb::embed_key_slots(N));
+    if (!ws || ws_bytes < need) return fail(MLB_E_ARENA_TOO_SMALL, "scatter of %ld positions needs %zu bytes", (long)N, need);
     const int r = mlb::embed_scatter(ids, dh, N, d, V, dE, dE, 0, static_cast<uint64_t*>(ws),
                                      static_cast<hipStream_t>(stream));
     return r == 0 ? MLB_OK : fail(MLB_E_INVALID_ARG, "embed_scatter (%d)", r);
@@ -1591,7 +1592,7 @@ mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N
 // array's name to a kernel (on the host it is only a stand-in symbol): its
 // device address is looked up once per device with hipGetSymbolAddress and
 // that address is what the kernels receive.
-constexpr int64_t SCATTER_SCRATCH_KEYS = MAX_TOKENS;   // 64 KiB of sort keys
+constexpr int64_t SCATTER_SCRATCH_KEYS = 8192;   // 64 KiB of sort keys
 static __device__ __align__(256) uint64_t scratch[SCATTER_SCRATCH_KEYS];
 
 namespace {

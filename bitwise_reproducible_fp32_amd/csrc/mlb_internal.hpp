@@ -164,7 +164,10 @@ int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s
 // Embedding-gradient scatter. For every row v that appears in ids, in order of
 // increasing position n: acc = init(v); acc = acc + dh[n]; then
 // dst[v] = acc (mode 0) or dst[v] = dst[v] + acc (mode 1). init(v) is +0 when
-// src_init is null, else src_init[v]. keys must hold 2*N uint64 values.
+// src_init is null, else src_init[v]. keys must hold embed_key_slots(N)
+// uint64 values; N is at most EMBED_MAX_POSITIONS.
+constexpr int64_t EMBED_MAX_POSITIONS = 65536;
+int64_t embed_key_slots(int64_t N);
 int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V,
                   const float* src_init, float* dst, int mode, uint64_t* keys, hipStream_t s);
 // The two halves of embed_scatter: the key sort (which depends on the ids

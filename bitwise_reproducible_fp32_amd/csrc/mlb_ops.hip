@@ -721,18 +721,21 @@ __global__ __launch_bounds__(64) void k_sum64(const float* __restrict__ v, int64
     if (lane == 0) out[0] = t * mul;
 }
 
-// Sort keys (id << 32 | n) in one workgroup (bitonic network in LDS). The keys
-// are distinct, so the sorted order is unique: ids ascending, positions
+// Sort keys (id << 32 | n) in LDS, one workgroup per block of P positions
+// (bitonic network; block b covers positions b*P .. b*P + P - 1, positions
+// past N and ids outside [0, V) become ~0 and sort last). The keys are
+// distinct, so each block's sorted order is unique: ids ascending, positions
 // ascending within an id.
 constexpr int SORT_MAX = 8192;   // 64 KiB of LDS keys
 __global__ __launch_bounds__(1024) void k_sort_keys(const int32_t* __restrict__ ids, int64_t N, int64_t V,
                                                     int64_t P, uint64_t* __restrict__ out) {
     __shared__ uint64_t key[SORT_MAX];
+    const int64_t base = (int64_t)blockIdx.x * P;
     for (int64_t q = threadIdx.x; q < P; q += blockDim.x) {
         uint64_t k = ~0ull;
-        if (q < N) {
-            const int32_t id = ids[q];
-            if (id >= 0 && id < V) k = ((uint64_t)(uint32_t)id << 32) | (uint64_t)q;
+        if (base + q < N) {
+            const int32_t id = ids[base + q];
+            if (id >= 0 && id < V) k = ((uint64_t)(uint32_t)id << 32) | (uint64_t)(base + q);
         }
         key[q] = k;
     }
@@ -752,7 +755,31 @@ __global__ __launch_bounds__(1024) void k_sort_keys(const int32_t* __restrict__ 
             __syncthreads();
         }
     }
-    for (int64_t q = threadIdx.x; q < P; q += blockDim.x) out[q] = key[q];
+    for (int64_t q = threadIdx.x; q < P; q += blockDim.x) out[base + q] = key[q];
+}
+
+// One pass of the merge sort above the LDS blocks: the sorted runs
+// in[2rL .. 2rL + L) and in[2rL + L .. 2rL + 2L) become one sorted run of 2L.
+// Each key goes to its rank: its index in its own run plus the count of keys
+// of the other run below it (first run) or at most it (second run), so equal
+// keys (only the ~0 fillers) keep the first run's ahead and every output slot
+// is written exactly once. total is a multiple of 2L.
+__global__ __launch_bounds__(256) void k_merge_runs(const uint64_t* __restrict__ in, uint64_t* __restrict__ out,
+                                                    int64_t L, int64_t total) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= total) return;
+    const int64_t base = g / (2 * L) * (2 * L), o = g - base;
+    const bool first = o < L;
+    const uint64_t x = in[g];
+    const uint64_t* other = in + base + (first ? L : 0);
+    int64_t lo = 0, hi = L;   // binary search for the count
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        const uint64_t y = other[mid];
+        if (first ? y < x : y <= x) lo = mid + 1;
+        else hi = mid;
+    }
+    out[base + (first ? o : o - L) + lo] = x;
 }
 
 // For each segment head q (first sorted key of an id): acc = init(v); for the
@@ -1154,22 +1181,44 @@ int sum64_scaled(const float* v, int64_t n, float mul, float* out, hipStream_t s
 
 static bool keys32(int64_t N, int64_t V) { return V < (1 << 19) - 1 && N <= SORT32_THREADS * SORT32_PER; }
 
+static int64_t pow2_at_least(int64_t n) {
+    int64_t p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
+int64_t embed_key_slots(int64_t N) { return N <= SORT_MAX ? SORT_MAX : 2 * pow2_at_least(N); }
+
 int embed_sort(const int32_t* ids, int64_t N, int64_t V, uint64_t* keys, hipStream_t s) {
-    if (N < 0 || V <= 0 || N > SORT_MAX) return -2;
+    if (N < 0 || V <= 0 || N > EMBED_MAX_POSITIONS) return -2;
     if (N == 0) return 0;
     if (keys32(N, V)) {
         k_sort_keys32<<<1, SORT32_THREADS, 0, s>>>(ids, N, V, reinterpret_cast<uint32_t*>(keys));
         return ok();
     }
-    int64_t P = 1;
-    while (P < N) P <<= 1;
-    k_sort_keys<<<1, 1024, 0, s>>>(ids, N, V, P, keys);
+    if (N <= SORT_MAX) {
+        k_sort_keys<<<1, 1024, 0, s>>>(ids, N, V, pow2_at_least(N), keys);
+        return ok();
+    }
+    // blocks of SORT_MAX sorted in LDS, then merge passes that double the run
+    // length, alternating between the two halves of keys so that the last
+    // pass writes the first half
+    const int64_t P = pow2_at_least(N);
+    int passes = 0;
+    for (int64_t L = SORT_MAX; L < P; L <<= 1) ++passes;
+    uint64_t* src = passes % 2 ? keys + P : keys;
+    uint64_t* dst = passes % 2 ? keys : keys + P;
+    k_sort_keys<<<(unsigned)(P / SORT_MAX), 1024, 0, s>>>(ids, N, V, SORT_MAX, src);
+    for (int64_t L = SORT_MAX; L < P; L <<= 1) {
+        k_merge_runs<<<(unsigned)(P / 256), 256, 0, s>>>(src, dst, L, P);
+        uint64_t* t = src; src = dst; dst = t;
+    }
     return ok();
 }
 
 int embed_scatter_sorted(const uint64_t* keys, const float* dh, int64_t N, int64_t d, int64_t V,
                          const float* src_init, float* dst, int mode, hipStream_t s) {
-    if (N < 0 || d <= 0 || V <= 0 || N > SORT_MAX) return -2;
+    if (N < 0 || d <= 0 || V <= 0 || N > EMBED_MAX_POSITIONS) return -2;
     if (N == 0) return 0;
     if (keys32(N, V))
         k_scatter_segments32<<<dim3((unsigned)N, blocks(d, 256)), 256, 0, s>>>(
@@ -1181,7 +1230,7 @@ int embed_scatter_sorted(const uint64_t* keys, const float* dh, int64_t N, int64
 
 int embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, const float* src_init,
                   float* dst, int mode, uint64_t* keys, hipStream_t s) {
-    if (N < 0 || d <= 0 || V <= 0 || N > SORT_MAX) return -2;
+    if (N < 0 || d <= 0 || V <= 0 || N > EMBED_MAX_POSITIONS) return -2;
     const int r = embed_sort(ids, N, V, keys, s);
     return r ? r : embed_scatter_sorted(keys, dh, N, d, V, src_init, dst, mode, s);
 }

@@ -48,7 +48,7 @@ typedef int32_t mlb_status;
 
 /* Model shape and optimiser constants. abi_version must be MLB_ABI_VERSION.
  * d_model = n_heads * head_dim; head_dim even; d_model and ffn_hidden multiples
- * of 32; batch * seq_len <= 8192 tokens per micro-batch. */
+ * of 32; batch * seq_len <= 65,536 tokens per micro-batch. */
 typedef struct mlb_config {
     uint32_t abi_version;
     uint32_t vocab, d_model, n_layers, n_heads, head_dim, ffn_hidden, tied, batch, seq_len;

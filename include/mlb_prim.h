@@ -102,8 +102,10 @@ mlb_status mlb_prim_cross_entropy(const float* logits, const int32_t* targets, i
 
 /* Embedding-gradient scatter (model card: the input table is a lookup): for
  * each row v, in increasing position n with ids[n] = v, dE[v] = dE[v] + dh[n]
- * (sorted segments, no floating-point atomics). N <= 8192; ids outside [0, V)
- * are skipped. ws: 2*8192*8 bytes. */
+ * (sorted segments, no floating-point atomics). N <= 65,536; ids outside
+ * [0, V) are skipped. ws: 131,072 bytes for N <= 8,192, else 16*P bytes with P
+ * the smallest power of two >= N (the sort keys and their merge buffer); a
+ * smaller ws gives MLB_E_ARENA_TOO_SMALL, a larger N MLB_E_UNSUPPORTED. */
 mlb_status mlb_prim_embed_scatter(const int32_t* ids, const float* dh, int64_t N, int64_t d, int64_t V, float* dE,
                                   void* ws, size_t ws_bytes, void* hip_stream);
 

@@ -63,7 +63,7 @@ def test_workspace_fits_the_162m_model(mlb):
     (dict(d_model=30), "MLB_E_INVALID_ARG"),          # heads * head_dim != d_model
     (dict(head_dim=7, n_heads=4, d_model=28), "MLB_E_UNSUPPORTED"),
     (dict(ffn_hidden=100), "MLB_E_UNSUPPORTED"),
-    (dict(batch=200), "MLB_E_UNSUPPORTED"),           # > 8192 tokens per micro-batch
+    (dict(batch=1025), "MLB_E_UNSUPPORTED"),          # > 65,536 tokens per micro-batch
     (dict(vocab=0), "MLB_E_INVALID_ARG"),
     (dict(rms_eps=float("nan")), "MLB_E_INVALID_ARG"),
 ])

@@ -515,6 +515,35 @@ def test_embed_scatter_zipf(mlb):
     assert_bits("dE", host(dE), want)
 
 
+@pytest.mark.parametrize("N", [8193, 20000, 65536])
+def test_embed_scatter_beyond_one_sort_block(mlb, N):
+    """More positions than one workgroup's LDS sort holds: blocks of 8,192
+    keys sorted in LDS, then one, two and three merge passes; a ragged last
+    block (8,193 and 20,000) is padded with keys that sort last."""
+    from bitwise_reproducible_fp32_amd import inputs as I
+    V, d = 50257, 257
+    ids = I.zipf_ids(N, V, N)
+    dh = make(np.random.default_rng(N + 1), (N, d))
+    base = make(np.random.default_rng(N + 2), (V, d))
+    want = oracle.embed_scatter(ids, dh, base)
+    P = 1 << (N - 1).bit_length()
+    dE = dev(base)
+    mlb.embed_scatter(dev(ids), dev(dh), N, d, V, dE, empty(4 * P))
+    assert_bits("dE", host(dE), want)
+
+
+def test_embed_scatter_limits(mlb):
+    ids = dev(np.zeros(65537, np.int32))
+    dh = empty(65537 * 4)
+    dE = empty(8 * 4)
+    with pytest.raises(mlb.MlbError) as e:               # more positions than the sort takes
+        mlb.embed_scatter(ids, dh, 65537, 4, 8, dE, empty(4 * 131072))
+    assert e.value.name == "MLB_E_UNSUPPORTED"
+    with pytest.raises(mlb.MlbError) as e:               # 20,000 positions need 16 * 32,768 bytes
+        mlb.embed_scatter(ids, dh, 20000, 4, 8, dE, empty(4 * 32768 - 1))
+    assert e.value.name == "MLB_E_ARENA_TOO_SMALL"
+
+
 def test_adamw(mlb):
     rng = np.random.default_rng(11)
     n = 1 << 20

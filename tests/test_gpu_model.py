@@ -80,6 +80,32 @@ def test_c0_first_step_stages_match_live_oracle():
         assert_bits(name, g.read(w), o.read(w))
 
 
+@pytest.mark.parametrize("batch", [160, 1024])
+def test_large_micro_batch_step_matches_oracle(batch):
+    """Micro-batches beyond one workgroup's LDS key sort (8,192 tokens): 10,240
+    tokens (two sorted blocks, one merge pass) and 65,536, the largest accepted
+    (eight blocks, three merge passes). The byte LM's 256 ids each appear
+    hundreds of times, so the embedding-gradient segments are long. Loss,
+    gradient and the state after AdamW equal the oracle's."""
+    import bitwise_reproducible_fp32_amd as mlb
+    cfg = I.make_config("c0", batch=batch)
+    p = I.init_params(cfg)
+    x, y = I.c0_batch(0, batch=batch)
+    g = mlb.Model(cfg, p)
+    o = oracle.Model(cfg, p)
+    try:
+        assert g.forward_loss(dev(x.astype(np.int32)), dev(y.astype(np.int32))).tobytes() == o.forward(x, y).tobytes()
+        g.backward()
+        o.backward()
+        assert_bits("G after one backward", g.read(mlb.GRAD), o.grad)
+        g.adamw_step(1e-3)
+        o.adamw(np.float32(1e-3))
+        for w, name in ((mlb.PARAMS, "params"), (mlb.ADAM_M, "m"), (mlb.ADAM_V, "v")):
+            assert_bits(name, g.read(w), o.read(w))
+    finally:
+        g.close()
+
+
 @pytest.mark.parametrize("overlap", [True, False])
 def test_c0_four_steps_bit_exact(overlap):
     """Both backward schedules (weight-gradient work on the side stream, or all
