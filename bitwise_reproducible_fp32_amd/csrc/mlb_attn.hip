@@ -471,10 +471,12 @@ void k_attn_rows(RowsArgs a) {
         const bool active = !(diag_tile && wc > wr);
         // this wave's 32x32 block of the tiled [T, T] layouts, and the lane's column in it
         const uint32_t blk = ((uint32_t)((i0 + rl) >> 5) * (uint32_t)ptr + (uint32_t)((j0 >> 5) + wc)) << 10;
+        // P is read once and S / dS written once: nontemporal, so that the
+        // streams do not push the strip, v and k tiles out of L2
         float pv[16];
         if (DS && active) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) pv[e] = Pz[blk + (uint32_t)(row_of(e) * 32 + li)];
+            for (int e = 0; e < 16; ++e) pv[e] = __builtin_nontemporal_load(Pz + (blk + (uint32_t)(row_of(e) * 32 + li)));
         }
         v16f acc;
 #pragma unroll
@@ -501,7 +503,7 @@ void k_attn_rows(RowsArgs a) {
             // read as a value (the softmax and every contraction take j <= i
             // only, and the exported P shows +0 there).
 #pragma unroll
-            for (int e = 0; e < 16; ++e) S[blk + (uint32_t)(row_of(e) * 32 + li)] = x[e];
+            for (int e = 0; e < 16; ++e) __builtin_nontemporal_store(x[e], S + (blk + (uint32_t)(row_of(e) * 32 + li)));
         }
         if (DS) {
             __syncthreads();                  // every wave is done with the v tile

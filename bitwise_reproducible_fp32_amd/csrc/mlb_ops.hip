@@ -415,8 +415,11 @@ __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int6
 // D_i = DOT64 over the head dimension of dO and O. A wavefront takes
 // ROWDOT_R consecutive rows (z, i) and, for heads of at most 64, loads all of
 // them before the first chain, so that more loads are in flight per wave; each
-// row is still its own lane chain and tree.
-constexpr int ROWDOT_R = 4;
+// row is still its own lane chain and tree. ONE_HEAD (T a multiple of
+// ROWDOT_R): a wave's rows are positions of one head, located by one division
+// per wave; otherwise each row is located on its own.
+constexpr int ROWDOT_R = 8;
+template <bool ONE_HEAD>
 __global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, const float* __restrict__ O,
                                                 int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
                                                 float* __restrict__ D) {
@@ -425,29 +428,32 @@ __global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, co
     const int64_t nrows = B * H * T;
     if (row0 >= nrows) return;
     auto offset = [&](int64_t row) -> int64_t {
-        const int64_t i = row % T, z = row / T, b = z / H, h = z % H;
-        return (b * T + i) * ld + h * hd;
+        const int64_t i = row % T, z = row / T;
+        return ((z / H) * T + i) * ld + (z % H) * hd;
     };
+    const int64_t off0 = offset(row0);
+    auto off_of = [&](int k) -> int64_t { return ONE_HEAD ? off0 + k * ld : offset(row0 + k); };
+    auto valid = [&](int k) -> bool { return ONE_HEAD || row0 + k < nrows; };
     if (hd <= 64) {
         float x[ROWDOT_R], y[ROWDOT_R];
+        const bool in = lane < hd;
 #pragma unroll
         for (int k = 0; k < ROWDOT_R; ++k) {
-            const int64_t row = row0 + k;
-            const bool in = row < nrows && lane < hd;
-            const int64_t off = in ? offset(row) + lane : 0;
-            x[k] = in ? dO[off] : 0.0f;
-            y[k] = in ? O[off] : 0.0f;
+            const bool use = in && valid(k);
+            const int64_t off = use ? off_of(k) + lane : 0;
+            x[k] = use ? dO[off] : 0.0f;
+            y[k] = use ? O[off] : 0.0f;
         }
 #pragma unroll
         for (int k = 0; k < ROWDOT_R; ++k) {
             // a lane past hd holds no element: its chain stays +0 (fma(0, 0, +0) is +0)
             const float t = wave_tree_sum(__builtin_fmaf(x[k], y[k], 0.0f));
-            if (lane == 0 && row0 + k < nrows) D[row0 + k] = t;
+            if (lane == 0 && valid(k)) D[row0 + k] = t;
         }
         return;
     }
-    for (int k = 0; k < ROWDOT_R && row0 + k < nrows; ++k) {
-        const int64_t off = offset(row0 + k);
+    for (int k = 0; k < ROWDOT_R && valid(k); ++k) {
+        const int64_t off = off_of(k);
         float acc = 0.0f;
         for (int64_t c = lane; c < hd; c += 64) acc = __builtin_fmaf(dO[off + c], O[off + c], acc);
         const float t = wave_tree_sum(acc);
@@ -1118,7 +1124,8 @@ int softmax_causal(float* P, int64_t nbh, int64_t T, int blk, hipStream_t s) {
 int attn_rowdot(const float* dO, const float* O, int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
                 float* D, hipStream_t s) {
     if (B * H * T == 0) return 0;
-    k_rowdot<<<blocks(B * H * T, 4 * ROWDOT_R), 256, 0, s>>>(dO, O, B, H, T, hd, ld, D);
+    if (T % ROWDOT_R == 0) k_rowdot<true><<<blocks(B * H * T, 4 * ROWDOT_R), 256, 0, s>>>(dO, O, B, H, T, hd, ld, D);
+    else k_rowdot<false><<<blocks(B * H * T, 4 * ROWDOT_R), 256, 0, s>>>(dO, O, B, H, T, hd, ld, D);
     return ok();
 }
 
