@@ -646,8 +646,13 @@ __global__ __launch_bounds__(64 * XR_W) void k_xent_row(const float* l_in, const
 #pragma unroll
     for (int c = 0; c < C; ++c)
         e[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rin, (vb + 64u * (uint32_t)c) * 4u, 0, 0));
+    // every position of a full wave is below V: its lanes skip the position
+    // tests (only the last wave of a row holds positions past V)
+    const bool full = (int64_t)64 * C * (w + 1) <= V;
+    if (!full) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) e[c] = c < nv ? e[c] : -__builtin_inff();
+        for (int c = 0; c < C; ++c) e[c] = c < nv ? e[c] : -__builtin_inff();
+    }
     // the position tests are made again below rather than kept as C lane masks
     asm volatile("" : "+v"(nv));
     float m = -__builtin_inff();
@@ -659,8 +664,13 @@ __global__ __launch_bounds__(64 * XR_W) void k_xent_row(const float* l_in, const
     m = wmax[0];
 #pragma unroll
     for (int k = 1; k < XR_W; ++k) m = max_keep(m, wmax[k]);
+    if (full) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) e[c] = exp_p_select(c < nv ? e[c] - m : -__builtin_inff());   // exp(-inf) = +0
+        for (int c = 0; c < C; ++c) e[c] = exp_p_select(e[c] - m);
+    } else {
+#pragma unroll
+        for (int c = 0; c < C; ++c) e[c] = exp_p_select(c < nv ? e[c] - m : -__builtin_inff());   // exp(-inf) = +0
+    }
     for (int k = 0; k < XR_W; ++k) {
         if (w == k) {
             float acc = k == 0 ? 0.0f : chain[lane];
@@ -676,11 +686,14 @@ __global__ __launch_bounds__(64 * XR_W) void k_xent_row(const float* l_in, const
     const float rz = 1.0f / Z;
     const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc((void*)(dl + n * ld), 0, (int)(V * 4), 0x00020000);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const float p = e[c] * rz;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((c == cy ? (p - 1.0f) : p) * invN), rout,
-                                              (vb + 64u * (uint32_t)c) * 4u, 0, 0);
-    }
+    for (int c = 0; c < C; ++c)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((e[c] * rz) * invN), rout, (vb + 64u * (uint32_t)c) * 4u,
+                                              0, 0);
+    // the target's entry, written again by the lane that holds it: its e is
+    // exp_p(l_y - m), recomputed from the same l_y (the same bits as e[cy])
+    if (cy >= 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(((exp_p_select(ly - m) * rz) - 1.0f) * invN), rout,
+                                              (vb + 64u * (uint32_t)cy) * 4u, 0, 0);
 }
 
 // Greedy choice, one wavefront per selected row r (row index r * row_step +
