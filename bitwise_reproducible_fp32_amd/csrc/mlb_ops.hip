@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_gather(const int32_t* __restrict__ ids,
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x, const float* __restrict__ w,
                                                      int64_t rows, int64_t d, float eps, float* __restrict__ y,
                                                      float* __restrict__ r) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const float* xr = x + row * d;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx(const float* __restrict__ dy, const float* __restrict__ x,
                                                         const float* __restrict__ w, const float* __restrict__ r,
                                                         int64_t rows, int64_t d, const float* base, float* out) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
     const float rr = r[row];
@@ -104,11 +104,14 @@ __device__ __forceinline__ void row_store(__amdgpu_buffer_rsrc_t rs, uint32_t c,
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, c * 4u, 0, 0);
 }
 
+// In these row kernels the row is taken as uniform across the wave
+// (readfirstlane): the row's buffer descriptors then sit in scalar registers,
+// and no access needs a loop over distinct descriptors.
 template <int E>
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd_reg(const float* __restrict__ x, const float* __restrict__ w,
                                                          int64_t rows, int64_t d, float eps, float* __restrict__ y,
                                                          float* __restrict__ r) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
     if (row >= rows) return;
     const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * d, d), rw = row_rsrc(w, d), ry = row_rsrc(y + row * d, d);
@@ -130,7 +133,7 @@ template <int E>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx_reg(const float* __restrict__ dy, const float* __restrict__ x,
                                                             const float* __restrict__ w, const float* __restrict__ r,
                                                             int64_t rows, int64_t d, const float* base, float* out) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t lane = threadIdx.x & 63;
     if (row >= rows) return;
     const float rr = r[row];
@@ -351,7 +354,7 @@ __device__ __forceinline__ float exp_p_select(float x) {
 // Causal softmax in place, one wavefront per row i over j <= i:
 // m = MAX64, e = exp(S - m), Z = SUM64(e), P = e * (1 / Z).
 __global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t T, int blk) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= nbh * T) return;
     const int64_t i = row % T;
@@ -374,42 +377,69 @@ __global__ __launch_bounds__(256) void k_softmax(float* P, int64_t nbh, int64_t 
 // The same rule with the row held in registers (lane l owns j = l + 64m,
 // m < PER): one read and one write of the row instead of three and two.
 // Element j = lane + 64 m of row i sits at base + m * stride inside the
-// head's matrix (tiled: two 32-wide tiles further per m), as an unsigned
-// 32-bit offset (T * T < 2^32): one address register per lane.
+// head's matrix (tiled: two 32-wide tiles further per m; T * T < 2^30).
 template <int PER>
 __global__ __launch_bounds__(256) void k_softmax_reg(float* P, int64_t nbh, int64_t T, int blk) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // the row is uniform across the wave: saying so keeps the row's pointer and
+    // buffer descriptor in scalar registers
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= nbh * T) return;
     const int64_t i = row % T;
     float* p = P + (row / T) * T * T;
     const int64_t n = i + 1;
-    const uint32_t base = (uint32_t)pos(blk, T, i, lane), stride = blk ? 2048u : 64u;
+    // this lane's count of positions j = lane + 64 m inside the row
+    int nvm = n > lane ? (int)((n - lane + 63) / 64) : 0;
+    uint32_t base = (uint32_t)pos(blk, T, i, lane) * 4u;
+    const uint32_t stride = (blk ? 2048u : 64u) * 4u;
+    // buffer accesses over the head's matrix: element m at the lane's byte
+    // offset plus m * stride (a scalar offset); positions past the row take an
+    // offset beyond the buffer, which loads +0 and drops the store, so no lane
+    // branches around a load or a store
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, (int)(T * T * 4), 0x00020000);
+    auto vo = [&](int m) -> uint32_t { return m < nvm ? base : 0x80000000u; };
+    // accesses past the row for every lane are not issued: the wave takes the
+    // smallest multiple of PER / 4 of them that covers its row (a scalar branch)
+    const int nw = (int)((n + 63) / 64);
+    constexpr int Q = PER / 4;
+    const int ng = (nw + Q - 1) / Q;   // 1 .. 4
     float v[PER];
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-        const int64_t j = lane + 64 * m;
-        v[m] = j < n ? p[base + (uint32_t)m * stride] : 0.0f;
-    }
+    for (int m = 0; m < PER; ++m) v[m] = 0.0f;
+    auto load_to = [&](auto cnt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < decltype(cnt)::value; ++m)
+            v[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, vo(m), (uint32_t)m * stride, 0));
+    };
+    if (ng <= 1) load_to(std::integral_constant<int, Q>{});
+    else if (ng == 2) load_to(std::integral_constant<int, 2 * Q>{});
+    else if (ng == 3) load_to(std::integral_constant<int, 3 * Q>{});
+    else load_to(std::integral_constant<int, 4 * Q>{});
     float mx = -__builtin_inff();
 #pragma unroll
     for (int m = 0; m < PER; ++m)
-        if (lane + 64 * m < n) mx = max_keep(mx, v[m]);
+        if (m < nvm) mx = max_keep(mx, v[m]);
     mx = wave_tree_max(mx);
     float acc = 0.0f;
 #pragma unroll
     for (int m = 0; m < PER; ++m)
-        if (lane + 64 * m < n) {
+        if (m < nvm) {
             v[m] = exp_p_select(v[m] - mx);
             acc = acc + v[m];
         }
     const float Z = wave_tree_sum(acc);
     const float rz = 1.0f / Z;
+    // the offsets are formed again here rather than kept in PER registers
+    asm volatile("" : "+v"(nvm), "+v"(base));
+    auto store_to = [&](auto cnt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < PER; ++m) {
-        const int64_t j = lane + 64 * m;
-        if (j < n) p[base + (uint32_t)m * stride] = v[m] * rz;
-    }
+        for (int m = 0; m < decltype(cnt)::value; ++m)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[m] * rz), rs, vo(m), (uint32_t)m * stride, 0);
+    };
+    if (ng <= 1) store_to(std::integral_constant<int, Q>{});
+    else if (ng == 2) store_to(std::integral_constant<int, 2 * Q>{});
+    else if (ng == 3) store_to(std::integral_constant<int, 3 * Q>{});
+    else store_to(std::integral_constant<int, 4 * Q>{});
 }
 
 // D_i = DOT64 over the head dimension of dO and O. A wavefront takes
@@ -423,7 +453,7 @@ template <bool ONE_HEAD>
 __global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ dO, const float* __restrict__ O,
                                                 int64_t B, int64_t H, int64_t T, int64_t hd, int64_t ld,
                                                 float* __restrict__ D) {
-    const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * ROWDOT_R;
+    const int64_t row0 = ((int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) * ROWDOT_R;
     const int lane = threadIdx.x & 63;
     const int64_t nrows = B * H * T;
     if (row0 >= nrows) return;
@@ -546,7 +576,7 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd4(const float* __restrict__ d
 __global__ __launch_bounds__(256) void k_xent(const float* l_in, const int32_t* __restrict__ tg, int64_t N,
                                               int64_t V, int64_t ld, float invN, float* __restrict__ loss_rows,
                                               float* dl, int* err) {
-    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (n >= N) return;
     const float* l = l_in + n * ld;
@@ -703,7 +733,7 @@ __global__ __launch_bounds__(64 * XR_W) void k_xent_row(const float* l_in, const
 // lower index on equal values); 0 when every entry is NaN.
 __global__ __launch_bounds__(256) void k_argmax_rows(const float* __restrict__ x, int64_t nsel, int64_t row_step,
                                                      int64_t row_off, int64_t ld, int64_t V, int32_t* out) {
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t r = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (r >= nsel) return;
     const float* row = x + (r * row_step + row_off) * ld;
