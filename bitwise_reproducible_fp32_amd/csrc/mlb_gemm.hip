@@ -557,7 +557,6 @@ __global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, i
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t MN = M * N, idx = q * 4;
     if (idx >= MN) return;
-    const float4* p4 = reinterpret_cast<const float4*>(part);
     const int64_t MN4 = MN / 4;
     typedef float v4f __attribute__((ext_vector_type(4)));
     const v4f* pv = reinterpret_cast<const v4f*>(part);
@@ -572,8 +571,10 @@ __global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, i
         for (int u = 0; u < 8; ++u)
             if (c0 + u < nch) { t.x = t.x + x[u].x; t.y = t.y + x[u].y; t.z = t.z + x[u].z; t.w = t.w + x[u].w; }
     }
-    const int64_t i = idx / N, j = idx % N;
-    float* c = a.C + i * a.ldc + j;
+    // rows stored contiguously (ldc == N): the output offset is idx itself,
+    // with no 64-bit division per thread
+    const int64_t o_ij = a.ldc == N ? idx : (idx / N) * a.ldc + idx % N;
+    float* c = a.C + o_ij;
     float4 r = t;
     if (a.mode == 1) {
         const float4 o = *reinterpret_cast<const float4*>(c);
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, i
     } else if (a.mode == 2) {
         r.x = t.x * a.scale; r.y = t.y * a.scale; r.z = t.z * a.scale; r.w = t.w * a.scale;
     } else if (a.mode == 3) {
-        const float4 o = *reinterpret_cast<const float4*>(a.R + i * a.ldc + j);
+        const float4 o = *reinterpret_cast<const float4*>(a.R + o_ij);
         r.x = o.x + t.x; r.y = o.y + t.y; r.z = o.z + t.z; r.w = o.w + t.w;
     }
     *reinterpret_cast<float4*>(c) = r;
