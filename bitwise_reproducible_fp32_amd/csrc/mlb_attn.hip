@@ -215,7 +215,7 @@ __device__ __forceinline__ void rope_bwd_block(float (&q)[16], float* buf, int l
     }
 }
 
-template <int KR>
+template <int KR, bool ROPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void k_attn_av(AvArgs a) {
     // KR 1: A(i, k) = P[i][k], held i-major (row stride 65: the lanes of a
@@ -345,7 +345,7 @@ void k_attn_av(AvArgs a) {
                 acc[e] = 0.0f;
                 tot[e] = 0.0f;
             }
-            if (a.rope_cos) rope_bwd_block(v, As, ALD, rl, wc, li, lk, t * AV + rl, a.rope_cos, a.rope_sin);
+            if (ROPE) rope_bwd_block(v, As, ALD, rl, wc, li, lk, t * AV + rl, a.rope_cos, a.rope_sin);
             const uint32_t co = (uint32_t)(t * AV + rl) * (uint32_t)a.ldc + (uint32_t)(32 * wc + li);
 #pragma unroll
             for (int e = 0; e < 16; ++e) C[co + (uint32_t)(8 * (e >> 2) + 4 * lk + (e & 3)) * (uint32_t)a.ldc] = v[e];
@@ -620,8 +620,11 @@ int attn_av(int kr, int64_t T, int64_t hd, int64_t batch, int64_t H, const float
     const int64_t npairs = (T / AV + 1) / 2;
     AvArgs a{T, H, npairs, P, sPb, sPh, B, ldb, sBb, sBh, C, ldc, sCb, sCh, rope_cos, rope_sin};
     const dim3 grid((unsigned)(npairs * batch));
-    if (kr == 1) k_attn_av<1><<<grid, 256, 0, s>>>(a);
-    else k_attn_av<2><<<grid, 256, 0, s>>>(a);
+    // the rotary exchange is compiled only into the instances that use it
+    if (kr == 1 && !rope_cos) k_attn_av<1, false><<<grid, 256, 0, s>>>(a);
+    else if (kr == 1) k_attn_av<1, true><<<grid, 256, 0, s>>>(a);
+    else if (!rope_cos) k_attn_av<2, false><<<grid, 256, 0, s>>>(a);
+    else k_attn_av<2, true><<<grid, 256, 0, s>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
