@@ -532,6 +532,41 @@ def test_embed_scatter_beyond_one_sort_block(mlb, N):
     assert_bits("dE", host(dE), want)
 
 
+def test_embed_scatter_vocabulary_beyond_32_bit_keys(mlb):
+    """Ids of 2^19 - 1 and more do not fit the 32-bit keys: one workgroup's
+    64-bit key sort (5,000 positions) and the 64-bit segment walk."""
+    from bitwise_reproducible_fp32_amd import inputs as I
+    N, V, d = 5000, 600000, 20
+    ids = I.zipf_ids(N, V, 9)
+    ids[::7] = V - 1 - ids[::7]                        # ids above 2^19 as well
+    dh = make(np.random.default_rng(10), (N, d))
+    base = make(np.random.default_rng(11), (V, d))
+    want = oracle.embed_scatter(ids, dh, base)
+    dE = dev(base)
+    mlb.embed_scatter(dev(ids), dev(dh), N, d, V, dE, empty(2 * 8192 * 2))
+    assert_bits("dE", host(dE), want)
+
+
+@pytest.mark.parametrize("N", [3000, 10000])
+def test_embed_scatter_skips_ids_outside_the_table(mlb, N):
+    """Ids below 0 or at V and beyond contribute nothing; the rest keep their
+    order (compared with the oracle's scatter of the valid positions alone),
+    on the 32-bit key path and the blocked 64-bit one."""
+    from bitwise_reproducible_fp32_amd import inputs as I
+    V, d = 50257, 33
+    rng = np.random.default_rng(N)
+    ids = I.zipf_ids(N, V, N + 3)
+    bad = rng.random(N) < 0.05
+    ids[bad] = rng.choice(np.array([-1, -7, V, V + 5, 2 ** 31 - 1], np.int32), bad.sum())
+    dh = make(rng, (N, d))
+    base = make(np.random.default_rng(N + 4), (V, d))
+    want = oracle.embed_scatter(ids[~bad], dh[~bad], base)
+    P = max(8192, 1 << (N - 1).bit_length())
+    dE = dev(base)
+    mlb.embed_scatter(dev(ids), dev(dh), N, d, V, dE, empty(4 * P))
+    assert_bits("dE", host(dE), want)
+
+
 def test_embed_scatter_limits(mlb):
     ids = dev(np.zeros(65537, np.int32))
     dh = empty(65537 * 4)
