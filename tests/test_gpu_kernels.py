@@ -487,6 +487,20 @@ def test_cross_entropy(mlb, N, V):
         logits[2, V - 1] = np.float32(9.0)
     if N > 3:
         logits[3] = np.float32(0.25)
+    # rows outside the kernel's in-range exp path: a NaN, a +inf, entries that
+    # underflow exp, and an entry exactly at exp's underflow threshold (relative
+    # to a zero maximum); then one just above it, which stays on that path
+    if N > 4:
+        logits[4, 5] = np.float32(np.nan)
+    if N > 5:
+        logits[5, V // 2] = np.float32(np.inf)
+    if N > 6:
+        logits[6, V // 3] = np.float32(200.0)
+    for r, bits in ((7, 0xC2CFF1B5), (8, 0xC2CFF1B4)):
+        if N > r:
+            logits[r] = -np.abs(logits[r]) * 10
+            logits[r, 1] = np.float32(0.0)
+            logits[r, 3] = np.array([bits], np.uint32).view(np.float32)[0]
     rows, dl, loss = empty(N), empty(N * V), empty(1)
     mlb.cross_entropy(dev(logits), dev(tg), N, V, rows, dl, loss)
     lo, ro, dlo = oracle.cross_entropy(logits, tg)
