@@ -551,15 +551,14 @@ __global__ __launch_bounds__(256) void k_fold(const float* __restrict__ part, in
 // The same fold for four adjacent outputs of a row per thread (N % 4 == 0,
 // 16-byte aligned partials and rows): float4 traffic, nontemporal loads (each
 // partial is read once), and the partials of up to 8 chunks loaded before the
-// first addition, which is still in chunk order.
-__global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, int64_t nch, int64_t M, int64_t N,
-                                               KArgs a) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// first addition, which is still in chunk order. Thread q takes outputs
+// 4q .. 4q + 3 of problem a.
+__device__ __forceinline__ void fold4_at(const KArgs& a, int64_t M, int64_t N, int64_t q) {
     const int64_t MN = M * N, idx = q * 4;
     if (idx >= MN) return;
-    const int64_t MN4 = MN / 4;
+    const int64_t MN4 = MN / 4, nch = a.nsplit;
     typedef float v4f __attribute__((ext_vector_type(4)));
-    const v4f* pv = reinterpret_cast<const v4f*>(part);
+    const v4f* pv = reinterpret_cast<const v4f*>(a.part);
     const v4f t0 = __builtin_nontemporal_load(pv + q);
     float4 t = make_float4(t0.x, t0.y, t0.z, t0.w);
     for (int64_t c0 = 1; c0 < nch; c0 += 8) {
@@ -586,6 +585,19 @@ __global__ __launch_bounds__(256) void k_fold4(const float* __restrict__ part, i
         r.x = o.x + t.x; r.y = o.y + t.y; r.z = o.z + t.z; r.w = o.w + t.w;
     }
     *reinterpret_cast<float4*>(c) = r;
+}
+
+__global__ __launch_bounds__(256) void k_fold4(int64_t M, int64_t N, KArgs a) {
+    fold4_at(a, M, N, (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+// The folds of the two problems of a paired launch in one grid: blocks below
+// b0 take problem 0, the others problem 1.
+__global__ __launch_bounds__(256) void k_fold4_pair(int64_t M0, int64_t N0, KArgs a0, int64_t M1, int64_t N1, KArgs a1,
+                                                    int64_t b0) {
+    const int64_t blk = blockIdx.x;
+    if (blk < b0) fold4_at(a0, M0, N0, blk * blockDim.x + threadIdx.x);
+    else fold4_at(a1, M1, N1, (blk - b0) * blockDim.x + threadIdx.x);
 }
 
 struct Cfg { int wm, wn; };
@@ -778,11 +790,14 @@ bool vec_loads(const GemmDesc& d) {
 
 // The split partials of a (already written) added in chunk order, then the
 // epilogue mode: the second kernel of the split path.
+bool fold_v4(const GemmDesc& d, const KArgs& a) {
+    return d.N % 4 == 0 && d.ldc % 4 == 0 && aligned16(d.C) && aligned16(a.part) && (d.mode != 3 || aligned16(d.R));
+}
+int64_t fold4_blocks(const GemmDesc& d) { return (d.M * d.N / 4 + 255) / 256; }
+
 void launch_fold(const GemmDesc& d, const KArgs& a, hipStream_t s) {
     const int64_t n = d.M * d.N;
-    const bool v4 = d.N % 4 == 0 && d.ldc % 4 == 0 && aligned16(d.C) && aligned16(a.part) &&
-                    (d.mode != 3 || aligned16(d.R));
-    if (v4) k_fold4<<<(unsigned)((n / 4 + 255) / 256), 256, 0, s>>>(a.part, a.nsplit, d.M, d.N, a);
+    if (fold_v4(d, a)) k_fold4<<<(unsigned)fold4_blocks(d), 256, 0, s>>>(d.M, d.N, a);
     else k_fold<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a.part, a.nsplit, d.M, d.N, a);
 }
 }  // namespace
@@ -930,13 +945,24 @@ int gemm_pair(const GemmDesc& d0, const GemmDesc& d1, const GemmPlan& p, hipStre
         char main_kernel[sizeof g_launched];
         std::memcpy(main_kernel, g_launched, sizeof g_launched);
         std::snprintf(g_launched, sizeof g_launched, "k_fold");
-        for (int i = 0; i < 2; ++i) {
-            const GemmDesc& d = i ? d1 : d0;
-            const KArgs& k = i ? b : a;
+        auto fold_bytes = [](const GemmDesc& d, const KArgs& k) {
+            return 4.0 * (double)(d.M * d.N) * (double)(k.nsplit + 1 + (d.mode == 1 || d.mode == 3 ? 1 : 0));
+        };
+        if (fold_v4(d0, a) && fold_v4(d1, b)) {   // both folds in one launch
             t.begin();
-            launch_fold(d, k, s);
-            t.end(0.0, 4.0 * (double)(d.M * d.N) * (double)(k.nsplit + 1 + (d.mode == 1 || d.mode == 3 ? 1 : 0)));
+            const int64_t b0 = fold4_blocks(d0);
+            k_fold4_pair<<<(unsigned)(b0 + fold4_blocks(d1)), 256, 0, s>>>(d0.M, d0.N, a, d1.M, d1.N, b, b0);
+            t.end(0.0, fold_bytes(d0, a) + fold_bytes(d1, b));
             if (hipGetLastError() != hipSuccess) return -3;
+        } else {
+            for (int i = 0; i < 2; ++i) {
+                const GemmDesc& d = i ? d1 : d0;
+                const KArgs& k = i ? b : a;
+                t.begin();
+                launch_fold(d, k, s);
+                t.end(0.0, fold_bytes(d, k));
+                if (hipGetLastError() != hipSuccess) return -3;
+            }
         }
         std::memcpy(g_launched, main_kernel, sizeof g_launched);
     }
