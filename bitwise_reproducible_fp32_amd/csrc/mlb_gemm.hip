@@ -315,7 +315,9 @@ void k_gemm(KArgs a0, KArgs a1) {
     const int j0l = wn * 64 + li, j1l = j0l + 32;
     // one 32-row block against the wave's two 32-column blocks, all 16 k-pairs
     auto full_block = [&](v16f& c0, v16f& c1, int rloc, int ko) {
-#pragma unroll 4
+        // eight k-pairs per pass: the LDS reads of the next four are issued
+        // while the current four's MFMAs run
+#pragma unroll 8
         for (int p = 0; p < 16; ++p) {
             const int kk = ko + 2 * p + lk;
             const float av = a_lds(rloc + li, kk);
