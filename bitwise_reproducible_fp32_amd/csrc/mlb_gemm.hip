@@ -392,7 +392,7 @@ void k_gemm(KArgs a0, KArgs a1) {
             dirty0 = dirty0 || st0 != 0;
             dirty1 = dirty1 || st1 != 0;
             if (RB == 2 && st0 == 1 && st1 == 1) {
-#pragma unroll 4
+#pragma unroll 8
                 for (int p = 0; p < 16; ++p) {
                     const int kk = ko + 2 * p + lk;
                     const float a0 = a_lds(r0 + li, kk);
