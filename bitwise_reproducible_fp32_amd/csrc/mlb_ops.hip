@@ -174,7 +174,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_dx_reg(const float* __restr
 // time: a workgroup owns DW_CW columns of one chunk, and its sixteen waves
 // stage DW_RB-row blocks of dy and x * r in LDS (two buffers) with the loads
 // of the block after next already in flight (two register sets), while the
-// first DW_CW lanes run the column chains through the staged block.
+// first DW_CW lanes run the column chains through the staged block. The LDS
+// blocks are column-major (one column's rows contiguous): a chain lane reads
+// four rows of each operand with one 16-byte LDS read, and the chain over a
+// full block is unrolled whole so that those reads run ahead of the fmas.
 constexpr int DW_RB = 256;
 constexpr int DW_CW = 32;      // columns (chains) per workgroup
 constexpr int DW_THREADS = 1024;
@@ -185,7 +188,9 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
                                                                float* __restrict__ part) {
     constexpr int RS = DW_THREADS / CW;   // rows covered by one pass of the threads
     constexpr int PER = DW_RB / RS;       // values of each array per thread per block
-    __shared__ float sy[2][DW_RB][CW + 1], sx[2][DW_RB][CW + 1];
+    constexpr int RP = DW_RB + 4;         // row pitch of a column: 16-byte aligned, a 4-bank offset per column
+    __shared__ __align__(16) float sy[2][CW][RP];
+    __shared__ __align__(16) float sx[2][CW][RP];
     const int tid = threadIdx.x, col = tid % CW, rsub = tid / CW;
     const int64_t c = (int64_t)blockIdx.x * CW + col;
     const bool live = c < d;
@@ -212,8 +217,8 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
         __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            sy[buf][rsub + RS * q][col] = vy[q];
-            sx[buf][rsub + RS * q][col] = vx[q] * vr[q];
+            sy[buf][col][rsub + RS * q] = vy[q];
+            sx[buf][col][rsub + RS * q] = vx[q] * vr[q];
         }
     };
     float acc = 0.0f;
@@ -222,10 +227,18 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
             const int64_t len = (n1 - n0 - b * DW_RB) < DW_RB ? (n1 - n0 - b * DW_RB) : DW_RB;
             const int buf = (int)(b & 1);
             if (len == DW_RB) {
-#pragma unroll 16
-                for (int k = 0; k < DW_RB; ++k) acc = __builtin_fmaf(sy[buf][k][col], sx[buf][k][col], acc);
+                const float4* y4 = reinterpret_cast<const float4*>(&sy[buf][col][0]);
+                const float4* x4 = reinterpret_cast<const float4*>(&sx[buf][col][0]);
+#pragma unroll
+                for (int k = 0; k < DW_RB / 4; ++k) {
+                    const float4 yv = y4[k], xv = x4[k];
+                    acc = __builtin_fmaf(yv.x, xv.x, acc);
+                    acc = __builtin_fmaf(yv.y, xv.y, acc);
+                    acc = __builtin_fmaf(yv.z, xv.z, acc);
+                    acc = __builtin_fmaf(yv.w, xv.w, acc);
+                }
             } else {
-                for (int k = 0; k < len; ++k) acc = __builtin_fmaf(sy[buf][k][col], sx[buf][k][col], acc);
+                for (int k = 0; k < len; ++k) acc = __builtin_fmaf(sy[buf][col][k], sx[buf][col][k], acc);
             }
         }
     };
