@@ -254,6 +254,7 @@ struct mlb_model {
     float* logits;
     Ring dh, dgu, dxn, dqkv;
     float *dA, *dO, *dP, *Dv, *gE, *split, *split_side, *dwpart;
+    int64_t* dw_offs;   // the norm gains' offsets in G, in the order of their partial slots
     int64_t split_n;
     uint64_t* keys;
     float* host_stage;   // pinned, 64 bytes
@@ -350,7 +351,10 @@ size_t carve(mlb_model* M, char* base) {
     M->split_n = split_floats(s);
     M->split = c.take<float>(M->split_n > 0 ? M->split_n : 1);
     M->split_side = c.take<float>(M->split_n > 0 ? M->split_n : 1);
-    M->dwpart = c.take<float>(((s.N + KCH - 1) / KCH) * s.d);
+    // every norm gain's chunk partials of one micro-batch (two per layer), folded
+    // into G together at the end of the backward
+    M->dwpart = c.take<float>(2 * s.L * ((s.N + KCH - 1) / KCH) * s.d);
+    M->dw_offs = c.take<int64_t>(2 * s.L);
     M->keys = c.take<uint64_t>(mlb::embed_key_slots(s.N));
     return c.off + ALIGN;
 }
@@ -693,6 +697,12 @@ mlb_status ring_read(mlb_model* M, Ring& r, int k) {
 // micro-batch, in call order (one side stream), so the bits do not depend on
 // how the two streams interleave. The side stream joins the caller's stream at
 // the end.
+// Partial slot k of the norm gains' chunk partials (k = 2l: the MLP norm of
+// layer l, 2l + 1: its attention norm).
+static float* dw_slot(mlb_model* M, int64_t k) {
+    return M->dwpart + k * ((M->s.N + KCH - 1) / KCH) * M->s.d;
+}
+
 mlb_status backward(mlb_model* M) {
     const Sizes& s = M->s;
     const bool two = M->overlap;
@@ -736,7 +746,7 @@ mlb_status backward(mlb_model* M) {
         RUN("gu_dx", x2);
         CHK(to_side());
         OP("rmsnorm_dw", f4 * (2 * N * d + N + d),
-           mlb::rmsnorm_bwd_dw(DXN.buf[kx2], M->hmid[l], M->r2[l], N, d, M->dwpart, M->G + M->o_w2[l], 1, ss));
+           mlb::rmsnorm_bwd_dw_parts(DXN.buf[kx2], M->hmid[l], M->r2[l], N, d, dw_slot(M, 2 * l), ss));
         CHK(ring_read(M, DXN, kx2));
         on_main();
         const int kh1 = (kh + 1) % 4;
@@ -800,7 +810,7 @@ mlb_status backward(mlb_model* M) {
         RUN("qkv_dx", x1);
         CHK(to_side());
         OP("rmsnorm_dw", f4 * (2 * N * d + N + d),
-           mlb::rmsnorm_bwd_dw(DXN.buf[kx1], M->h[l], M->r1[l], N, d, M->dwpart, M->G + M->o_w1[l], 1, ss));
+           mlb::rmsnorm_bwd_dw_parts(DXN.buf[kx1], M->h[l], M->r1[l], N, d, dw_slot(M, 2 * l + 1), ss));
         CHK(ring_read(M, DXN, kx1));
         on_main();
         const int kh2 = (kh1 + 1) % 4;
@@ -820,6 +830,10 @@ mlb_status backward(mlb_model* M) {
         OP("embed_scatter", f4 * 3 * N * d,
            mlb::embed_scatter_sorted(M->keys, DH.buf[kh], N, d, s.V, nullptr, M->G + M->offE, 1, ss));
     }
+    // the norm gains: each micro-batch's chunk partials folded in chunk order
+    // and added to G (each gain's slice of G takes no other update)
+    OP("rmsnorm_dw_fold", f4 * (2 * s.L) * d * ((N + KCH - 1) / KCH + 2),
+       mlb::fold_cols_batched(M->dwpart, N, d, 2 * s.L, M->dw_offs, M->G, ss));
     // join: the caller's stream continues after all side work
     on_main();
     if (two) CHK(stream_wait(M, ss, st));
@@ -904,6 +918,12 @@ mlb_status mlb_init(const mlb_config* cfg, uint64_t seed, const float* init, voi
     step(hipMemcpyAsync(M->p, init, (size_t)M->s.P * 4, hipMemcpyHostToDevice, st), "upload params");
     step(hipMemcpyAsync(M->cosv, c.data(), c.size() * 4, hipMemcpyHostToDevice, st), "upload rope");
     step(hipMemcpyAsync(M->sinv, sn.data(), sn.size() * 4, hipMemcpyHostToDevice, st), "upload rope");
+    std::vector<int64_t> offs;
+    for (int64_t l = 0; l < M->s.L; ++l) {
+        offs.push_back(M->o_w2[l]);
+        offs.push_back(M->o_w1[l]);
+    }
+    step(hipMemcpyAsync(M->dw_offs, offs.data(), offs.size() * 8, hipMemcpyHostToDevice, st), "upload gain offsets");
     if (rc == MLB_OK) {
         if (mlb::fill_zero(M->G, M->s.P, st) || mlb::fill_zero(M->m, M->s.P, st) || mlb::fill_zero(M->v, M->s.P, st))
             rc = fail(MLB_E_DEVICE, "zero fill");

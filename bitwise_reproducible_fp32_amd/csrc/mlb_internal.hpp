@@ -138,6 +138,14 @@ int rmsnorm_bwd_dx(const float* dy, const float* x, const float* w, const float*
 // 1024 rows. part must hold ceil(rows/1024)*d floats. mode 0 dw = t, 1 dw = dw + t.
 int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows, int64_t d, float* part,
                    float* dw, int mode, hipStream_t s);
+// The gain gradient in two parts: the per-chunk column partials of one RMSNorm
+// (ceil(rows/1024) * d floats at part), and later, in one launch for nprob
+// of them, their folds in chunk order added to base + offs[p] (offs in device
+// memory, the partials of problem p at part + p * ceil(rows/1024) * d).
+int rmsnorm_bwd_dw_parts(const float* dy, const float* x, const float* r, int64_t rows, int64_t d, float* part,
+                         hipStream_t s);
+int fold_cols_batched(const float* part, int64_t rows, int64_t d, int64_t nprob, const int64_t* offs, float* base,
+                      hipStream_t s);
 int rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld, const float* cosv,
          const float* sinv, int backward, hipStream_t s);
 // In-place causal softmax of rows i of [nbh, T, T] over j <= i (blk: tiled

@@ -278,6 +278,20 @@ __global__ __launch_bounds__(256) void k_fold_cols(const float* __restrict__ par
     dw[c] = mode ? dw[c] + t : t;
 }
 
+// The folds of nprob gain gradients in one launch (problem p: partials at
+// part + p * nch * d, output at base + offs[p]), each dw[c] = dw[c] + t with
+// t the chunk partials added in chunk order, as k_fold_cols in mode 1.
+__global__ __launch_bounds__(256) void k_fold_cols_batched(const float* __restrict__ part, int64_t nch, int64_t d,
+                                                           const int64_t* __restrict__ offs, float* base) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= d) return;
+    const float* pp = part + (int64_t)blockIdx.y * nch * d;
+    float t = pp[c];
+    for (int64_t ch = 1; ch < nch; ++ch) t = t + pp[ch * d + c];
+    float* dw = base + offs[blockIdx.y];
+    dw[c] = dw[c] + t;
+}
+
 // Rotary embedding, half-split pairing (element i with i + hd/2) at position
 // t = n mod T, table values cos/sin[t][i].
 __global__ __launch_bounds__(256) void k_rope(float* x, int64_t B, int64_t T, int64_t H, int64_t hd, int64_t ld,
@@ -1150,6 +1164,22 @@ int rmsnorm_bwd_dw(const float* dy, const float* x, const float* r, int64_t rows
     const int64_t nch = (rows + KC - 1) / KC;
     k_rmsnorm_dw_part<DW_CW><<<dim3(blocks(d, DW_CW), (unsigned)nch), DW_THREADS, 0, s>>>(dy, x, r, rows, d, part);
     k_fold_cols<<<blocks(d, 256), 256, 0, s>>>(part, nch, d, dw, mode);
+    return ok();
+}
+
+int rmsnorm_bwd_dw_parts(const float* dy, const float* x, const float* r, int64_t rows, int64_t d, float* part,
+                         hipStream_t s) {
+    if (rows <= 0 || d <= 0) return -1;
+    const int64_t nch = (rows + KC - 1) / KC;
+    k_rmsnorm_dw_part<DW_CW><<<dim3(blocks(d, DW_CW), (unsigned)nch), DW_THREADS, 0, s>>>(dy, x, r, rows, d, part);
+    return ok();
+}
+
+int fold_cols_batched(const float* part, int64_t rows, int64_t d, int64_t nprob, const int64_t* offs, float* base,
+                      hipStream_t s) {
+    if (rows <= 0 || d <= 0 || nprob <= 0 || nprob > 65535) return -1;
+    const int64_t nch = (rows + KC - 1) / KC;
+    k_fold_cols_batched<<<dim3(blocks(d, 256), (unsigned)nprob), 256, 0, s>>>(part, nch, d, offs, base);
     return ok();
 }
 
