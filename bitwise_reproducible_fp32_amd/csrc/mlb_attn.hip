@@ -412,20 +412,23 @@ void k_attn_rows(RowsArgs a) {
     float rx[16], ry[16], rk[16];
     // Addresses are a workgroup-uniform base plus an unsigned 32-bit lane
     // offset (every per-head offset is below 2^32 / 4): one VGPR per address.
+    // float4 s of thread tid: row (tid >> 3) + 32 (s & 1), columns 4 ((tid & 7) + 8 (s >> 1)) .. + 3
+    // (a wave moves 8 rows x 8 float4: whole 128-byte lines from memory, and a
+    // half-wave's LDS stores of one element cover 4 rows x 32 columns, 32 banks)
     auto load_rows = [&](const float* base, uint32_t ld, uint32_t r0, float* dst) __attribute__((always_inline)) {
-        const uint32_t o = (r0 + (uint32_t)(tid >> 4)) * ld + (uint32_t)(tid & 15) * 4;
+        const uint32_t o = (r0 + (uint32_t)(tid >> 3)) * ld + (uint32_t)(tid & 7) * 4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float4 v = *reinterpret_cast<const float4*>(base + (o + 16u * (uint32_t)s * ld));
+            const float4 v = *reinterpret_cast<const float4*>(base + (o + 32u * (uint32_t)(s & 1) * ld + 32u * (uint32_t)(s >> 1)));
             dst[4 * s + 0] = v.x; dst[4 * s + 1] = v.y; dst[4 * s + 2] = v.z; dst[4 * s + 3] = v.w;
         }
     };
     auto put_rows = [&](float* dst, const float* src) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int q = tid + 256 * s;
+            const int r = (tid >> 3) + 32 * (s & 1), c = 4 * ((tid & 7) + 8 * (s >> 1));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(q >> 4) * LR + (q & 15) * 4 + e] = src[4 * s + e];
+            for (int e = 0; e < 4; ++e) dst[r * LR + c + e] = src[4 * s + e];
         }
     };
     auto tile_of = [&](int64_t st, int64_t& t, int64_t& sl) __attribute__((always_inline)) {
