@@ -189,6 +189,7 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
     constexpr int RS = DW_THREADS / CW;   // rows covered by one pass of the threads
     constexpr int PER = DW_RB / RS;       // values of each array per thread per block
     constexpr int RP = DW_RB + 4;         // row pitch of a column: 16-byte aligned, a 4-bank offset per column
+    static_assert(PER % 4 == 0, "four consecutive rows per thread and array");
     __shared__ __align__(16) float sy[2][CW][RP];
     __shared__ __align__(16) float sx[2][CW][RP];
     const int tid = threadIdx.x, col = tid % CW, rsub = tid / CW;
@@ -197,7 +198,9 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
     const int64_t n0 = (int64_t)blockIdx.y * KC, n1 = (n0 + KC < rows) ? n0 + KC : rows;
     const int64_t nb = (n1 - n0 + DW_RB - 1) / DW_RB;
     // raw loads (x * r is formed at the LDS store, so that nothing waits for
-    // a load before the block after next is issued)
+    // a load before the block after next is issued); thread (col, rsub) holds
+    // rows 4 RS h + 4 rsub + j, j < 4, of each block, and stores each four as
+    // one 16-byte LDS write (eight lanes' writes cover the 32 banks)
     float ya[PER], xa[PER], ra[PER], yb[PER], xb[PER], rb[PER];
     // Unconditional loads from clamped positions (a guarded load became a
     // branch with a wait per row): rows past the chunk are never taken by
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
     auto load = [&](int64_t b, float (&vy)[PER], float (&vx)[PER], float (&vr)[PER]) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            int64_t n = n0 + b * DW_RB + rsub + RS * q;
+            int64_t n = n0 + b * DW_RB + 4 * RS * (q >> 2) + 4 * rsub + (q & 3);
             n = n < n1 ? n : n1 - 1;
             vy[q] = dy[n * d + cc];
             vx[q] = x[n * d + cc];
@@ -216,9 +219,13 @@ __global__ __launch_bounds__(DW_THREADS) void k_rmsnorm_dw_part(const float* __r
     auto store = [&](int buf, const float (&vy)[PER], const float (&vx)[PER], const float (&vr)[PER])
         __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            sy[buf][col][rsub + RS * q] = vy[q];
-            sx[buf][col][rsub + RS * q] = vx[q] * vr[q];
+        for (int h = 0; h < PER / 4; ++h) {
+            const int o = 4 * RS * h + 4 * rsub;
+            *reinterpret_cast<float4*>(&sy[buf][col][o]) =
+                make_float4(vy[4 * h], vy[4 * h + 1], vy[4 * h + 2], vy[4 * h + 3]);
+            *reinterpret_cast<float4*>(&sx[buf][col][o]) =
+                make_float4(vx[4 * h] * vr[4 * h], vx[4 * h + 1] * vr[4 * h + 1], vx[4 * h + 2] * vr[4 * h + 2],
+                            vx[4 * h + 3] * vr[4 * h + 3]);
         }
     };
     float acc = 0.0f;
